@@ -1,0 +1,326 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself (closed forms, a textbook special case, brute force, invariants of
+the definition, the tiled recurrence, library decoders, page-given counts).
+
+The definition being pinned is softmax(Q K^T * scale) V with a per-row
+natural-log log-sum-exp, on [B][N][H][d] tensors ("FlashAttention-4 no
+Blackwell B200 ...", section "Por que o Blackwell exige mais do que
+multiplicações rápidas"; layout from the usage example of "FlashAttention-3:
+Pipeline Assíncrono ...", section "Implementando FlashAttention-3 em
+produção").
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import (attention_brute, attention_forward, attention_head_rows,
+                    bf16_bits_to_float64, dequantize_e4m3, e4m3fn_bits_to_float64,
+                    simulator_counts, tiled_online_softmax_head)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_queries_give_mean_of_visible_values(causal):
+    """Q = 0: every visible score is 0, so o_i is the plain mean of the
+    visible v_j and lse_i = ln(number of visible keys)."""
+    B, N, H, d = 2, 37, 3, 8
+    q = np.zeros((B, N, H, d))
+    k = _rand((B, N, H, d), 1)
+    v = _rand((B, N, H, d), 2)
+    o, lse = attention_forward(q, k, v, 0.3, causal)
+    for i in range(N):
+        n_vis = i + 1 if causal else N
+        np.testing.assert_allclose(o[:, i], v[:, :n_vis].mean(axis=1), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[:, :, i], math.log(n_vis), rtol=0, atol=1e-13)
+
+
+def test_equal_key_rows_give_mean_and_shifted_lse():
+    """All K rows equal: row i's scores all equal s_i = scale*q_i.k, so
+    o_i = mean of V over keys and lse_i = s_i + ln N."""
+    B, N, H, d = 1, 29, 2, 16
+    q = _rand((B, N, H, d), 3)
+    krow = _rand((B, 1, H, d), 4)
+    k = np.repeat(krow, N, axis=1)
+    v = _rand((B, N, H, d), 5)
+    scale = 0.25
+    o, lse = attention_forward(q, k, v, scale, False)
+    for b in range(B):
+        for h in range(H):
+            s = scale * q[b, :, h, :] @ krow[b, 0, h, :]
+            np.testing.assert_allclose(lse[b, h], s + math.log(N), rtol=0, atol=1e-12)
+            np.testing.assert_allclose(o[b, :, h, :], np.broadcast_to(v[b, :, h, :].mean(0), (N, d)),
+                                       rtol=0, atol=1e-13)
+
+
+def test_single_dominant_key_returns_its_value_row():
+    """k_{j*} = lambda * q_i with lambda large: o_i -> v_{j*}; the error is at
+    most (n-1) * exp(-margin) * 2 max|v| where margin is the score gap."""
+    N, d = 64, 32
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((N, d))
+    k = rng.standard_normal((N, d)) * 0.1
+    v = rng.standard_normal((N, d))
+    i, jstar = 17, 41
+    k[jstar] = 12.0 * q[i]
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attention_head_rows(q, k, v, scale, False, rows=[i])
+    s = scale * (k @ q[i])
+    margin = s[jstar] - np.max(np.delete(s, jstar))
+    assert margin > 30
+    bound = (N - 1) * math.exp(-margin) * 2 * np.abs(v).max()
+    assert np.abs(o[0] - v[jstar]).max() <= bound + 1e-15
+    assert abs(lse[0] - s[jstar]) <= (N - 1) * math.exp(-margin) + 1e-13
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    """With V = all ones, o_i = sum_j p_ij = 1; and sum_j exp(s_ij - lse_i) = 1
+    over the visible keys (ties lse to the scores)."""
+    B, N, H, d = 1, 50, 2, 8
+    q = _rand((B, N, H, d), 7, 2.0)
+    k = _rand((B, N, H, d), 8, 2.0)
+    o, lse = attention_forward(q, k, np.ones((B, N, H, d)), 0.7, causal)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-14)
+    for h in range(H):
+        for i in range(N):
+            js = range(i + 1) if causal else range(N)
+            tot = math.fsum(math.exp(0.7 * float(q[0, i, h] @ k[0, j, h]) - lse[0, h, i]) for j in js)
+            assert abs(tot - 1.0) < 1e-13
+
+
+def test_causal_row_zero_is_first_value_row():
+    """Causal: query 0 sees only key 0, so o_0 = v_0 exactly and
+    lse_0 = scale * q_0 . k_0."""
+    B, N, H, d = 2, 20, 3, 16
+    q = _rand((B, N, H, d), 9)
+    k = _rand((B, N, H, d), 10)
+    v = _rand((B, N, H, d), 11)
+    o, lse = attention_forward(q, k, v, 0.125, True)
+    np.testing.assert_array_equal(o[:, 0], v[:, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.125 * np.einsum("bhd,bhd->bh", q[:, 0], k[:, 0]),
+                               rtol=0, atol=1e-14)
+
+
+def test_two_keys_logistic_weights():
+    """N = 2, non-causal: the weights are logistic functions of the score
+    difference, o_i = sigma(s_i0 - s_i1) v_0 + sigma(s_i1 - s_i0) v_1."""
+    N, d = 2, 8
+    q = _rand((N, d), 12, 3.0)
+    k = _rand((N, d), 13, 3.0)
+    v = _rand((N, d), 14)
+    scale = 0.4
+    o, lse = attention_head_rows(q, k, v, scale, False)
+    for i in range(N):
+        s0 = scale * q[i] @ k[0]
+        s1 = scale * q[i] @ k[1]
+        w0 = 1.0 / (1.0 + math.exp(s1 - s0))
+        w1 = 1.0 / (1.0 + math.exp(s0 - s1))
+        np.testing.assert_allclose(o[i], w0 * v[0] + w1 * v[1], rtol=0, atol=1e-14)
+        assert abs(lse[i] - (max(s0, s1) + math.log1p(math.exp(-abs(s0 - s1))))) < 1e-14
+
+
+def test_huge_scale_is_hard_argmax():
+    """scale -> large: the softmax becomes a one-hot on each row's best key."""
+    N, d = 40, 8
+    q = _rand((N, d), 15)
+    k = _rand((N, d), 16)
+    v = _rand((N, d), 17)
+    o, _ = attention_head_rows(q, k, v, 1e4, False)
+    best = np.argmax(q @ k.T, axis=1)
+    np.testing.assert_allclose(o, v[best], rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# brute force
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1, 1), (1, 5, 2, 3), (2, 16, 2, 8), (1, 13, 3, 4)])
+def test_brute_force_agrees(shape, causal):
+    q = _rand(shape, 18, 1.5)
+    k = _rand(shape, 19, 1.5)
+    v = _rand(shape, 20)
+    scale = 1.0 / math.sqrt(shape[3])
+    o, lse = attention_forward(q, k, v, scale, causal)
+    ob, lb = attention_brute(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+    np.testing.assert_allclose(o, np.array(ob), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, np.array(lb), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# invariants
+# --------------------------------------------------------------------------
+
+def test_key_value_permutation_invariance():
+    """Non-causal attention does not depend on the order of the key/value
+    rows (permuting K and V together)."""
+    B, N, H, d = 1, 33, 2, 8
+    q, k, v = (_rand((B, N, H, d), s) for s in (21, 22, 23))
+    perm = np.random.default_rng(24).permutation(N)
+    o1, l1 = attention_forward(q, k, v, 0.5, False)
+    o2, l2 = attention_forward(q, k[:, perm], v[:, perm], 0.5, False)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_in_values(causal):
+    B, N, H, d = 1, 24, 2, 8
+    q, k, v1, v2 = (_rand((B, N, H, d), s) for s in (25, 26, 27, 28))
+    o1, _ = attention_forward(q, k, v1, 0.5, causal)
+    o2, _ = attention_forward(q, k, v2, 0.5, causal)
+    o3, _ = attention_forward(q, k, 2.0 * v1 - 3.0 * v2, 0.5, causal)
+    np.testing.assert_allclose(o3, 2.0 * o1 - 3.0 * o2, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_convexity_and_lse_bounds(causal):
+    """Each o_i lies between the column-wise min and max of the visible v_j,
+    and max_j s_ij <= lse_i <= max_j s_ij + ln(n_visible)."""
+    B, N, H, d = 1, 40, 2, 8
+    q, k, v = (_rand((B, N, H, d), s, 2.0) for s in (29, 30, 31))
+    scale = 0.5
+    o, lse = attention_forward(q, k, v, scale, causal)
+    for h in range(H):
+        s = scale * q[0, :, h] @ k[0, :, h].T
+        for i in range(N):
+            n = i + 1 if causal else N
+            vis = v[0, :n, h]
+            assert np.all(o[0, i, h] >= vis.min(0) - 1e-13)
+            assert np.all(o[0, i, h] <= vis.max(0) + 1e-13)
+            smax = s[i, :n].max()
+            assert smax - 1e-13 <= lse[0, h, i] <= smax + math.log(n) + 1e-13
+
+
+def test_row_shift_invariance():
+    """Adding the same amount to every score of a row (k_j -> k_j + u) leaves
+    o_i unchanged and shifts lse_i by scale * q_i . u."""
+    B, N, H, d = 1, 30, 1, 8
+    q, k, v = (_rand((B, N, H, d), s) for s in (32, 33, 34))
+    u = _rand((d,), 35)
+    scale = 0.6
+    o1, l1 = attention_forward(q, k, v, scale, False)
+    o2, l2 = attention_forward(q, k + u, v, scale, False)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2 - l1, scale * (q[0, :, 0] @ u)[None, None, :], rtol=0, atol=1e-12)
+
+
+def test_heads_and_batches_are_independent_in_bnhd_layout():
+    """Swapping two heads (axis 2) and two batches (axis 0) of Q, K, V swaps
+    the same slices of O and LSE; N is axis 1."""
+    B, N, H, d = 2, 18, 3, 8
+    q, k, v = (_rand((B, N, H, d), s) for s in (36, 37, 38))
+    o, lse = attention_forward(q, k, v, 0.5, True)
+    hp = [2, 0, 1]
+    bp = [1, 0]
+    o2, lse2 = attention_forward(q[bp][:, :, hp], k[bp][:, :, hp], v[bp][:, :, hp], 0.5, True)
+    np.testing.assert_allclose(o2, o[bp][:, :, hp], rtol=0, atol=0)
+    np.testing.assert_allclose(lse2, lse[bp][:, hp], rtol=0, atol=0)
+
+
+def test_row_subset_matches_full():
+    B, N, H, d = 1, 70, 2, 8
+    q, k, v = (_rand((B, N, H, d), s) for s in (39, 40, 41))
+    o, lse = attention_forward(q, k, v, 0.3, True)
+    rows = np.array([[[0, 69, 5, 33], [12, 1, 68, 40]]])
+    orow, lrow = attention_forward(q, k, v, 0.3, True, rows=rows)
+    for h in range(H):
+        np.testing.assert_allclose(orow[0, h], o[0, rows[0, h], h], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lrow[0, h], lse[0, h, rows[0, h]], rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# tiled recurrence (exactness of the online softmax)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bk", [1, 7, 32, 64])
+@pytest.mark.parametrize("tau", [0.0, 8.0 * math.log(2.0), math.inf])
+def test_tiled_equals_untiled(causal, bk, tau):
+    N, d = 150, 16
+    q, k, v = (_rand((N, d), s, 1.5) for s in (42, 43, 44))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attention_head_rows(q, k, v, scale, causal)
+    ot, lt, _ = tiled_online_softmax_head(q, k, v, scale, causal, 32, bk, tau)
+    np.testing.assert_allclose(ot, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lt, lse, rtol=0, atol=1e-12)
+
+
+def test_threshold_reduces_rescales_on_peaked_keys():
+    """Informative (the pages report ~10x fewer rescales for the adaptive
+    rule); here only the direction is asserted: a positive threshold never
+    rescales more often than the always-rescale rule."""
+    N, d = 1024, 32
+    rng = np.random.default_rng(45)
+    q = rng.standard_normal((N, d))
+    k = rng.standard_normal((N, d))
+    k[rng.choice(N, 10, replace=False)] *= 8.0
+    v = rng.standard_normal((N, d))
+    scale = 1.0 / math.sqrt(d)
+    _, _, s0 = tiled_online_softmax_head(q, k, v, scale, True, 128, 64, 0.0)
+    _, _, s8 = tiled_online_softmax_head(q, k, v, scale, True, 128, 64, 8.0 * math.log(2.0))
+    assert s8["rescales"] <= s0["rescales"]
+    assert s0["rescales"] > 0
+
+
+def test_simulator_counts_match_page():
+    with open(os.path.join(GOLDEN, "simulator_counts.json")) as f:
+        g = json.load(f)
+    got = simulator_counts(**g["inputs"])
+    assert got == g["expected"]
+
+
+# --------------------------------------------------------------------------
+# input-format decoders
+# --------------------------------------------------------------------------
+
+def test_e4m3_decoder_matches_library_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3fn_bits_to_float64(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], lib[~nan])
+
+
+def test_e4m3_decoder_known_values():
+    vals = e4m3fn_bits_to_float64(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0xB8, 0x7E, 0xFE, 0x7F, 0x80],
+                                           dtype=np.uint8))
+    exp = [0.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.0, -1.0, 448.0, -448.0]
+    np.testing.assert_array_equal(vals[:8], exp)
+    assert np.isnan(vals[8])
+    assert vals[9] == 0.0 and math.copysign(1.0, vals[9]) == -1.0
+
+
+def test_bf16_decoder_matches_library():
+    bits = np.random.default_rng(46).integers(0, 1 << 16, 4096, dtype=np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]           # drop inf/nan patterns
+    ours = bf16_bits_to_float64(bits)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, lib)
+    one = bf16_bits_to_float64(np.array([0x3F80, 0xC000, 0x0000], dtype=np.uint16))
+    np.testing.assert_array_equal(one, [1.0, -2.0, 0.0])
+
+
+def test_dequantize_uses_per_batch_head_descale():
+    B, N, H, d = 2, 3, 2, 4
+    codes = np.full((B, N, H, d), 0x38, dtype=np.uint8)     # 1.0
+    ds = np.array([[0.5, 2.0], [3.0, 0.25]], dtype=np.float32)
+    x = dequantize_e4m3(codes, ds)
+    for b in range(B):
+        for h in range(H):
+            assert np.all(x[b, :, h, :] == ds[b, h])

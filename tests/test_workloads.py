@@ -1,0 +1,64 @@
+"""The seeded input generator: reproducible, right shapes and structure."""
+
+import numpy as np
+import torch
+
+from oracle import bf16_bits_to_float64, dequantize_e4m3
+from workloads import WORKLOADS, Workload, make_bf16, make_fp8, sample_rows
+
+
+def test_bf16_inputs_are_seeded_and_shaped():
+    w = WORKLOADS["tiny"]
+    a = make_bf16(w)
+    b = make_bf16(w)
+    for name in "qkv":
+        assert a[name].dtype == np.uint16
+        assert a[name].shape == (w.B, w.N, w.H, w.d)
+        np.testing.assert_array_equal(a[name], b[name])
+    assert not np.array_equal(a["q"], a["k"])
+    x = bf16_bits_to_float64(a["q"])
+    assert abs(x.mean()) < 0.05 and abs(x.std() - 1.0) < 0.05
+
+
+def test_peaked_rows_are_one_percent_times_eight():
+    w = Workload("peak", 99, 1, 2, 1000, 16, "bf16", (True,), peaked_k=True)
+    base = Workload("plain", 99, 1, 2, 1000, 16, "bf16", (True,))
+    kp = bf16_bits_to_float64(make_bf16(w)["k"])
+    k0 = bf16_bits_to_float64(make_bf16(base)["k"])
+    for h in range(2):
+        ratio = np.abs(kp[0, :, h, :]).sum(1) / np.abs(k0[0, :, h, :]).sum(1)
+        peaked = np.isclose(ratio, 8.0, rtol=1e-2)
+        assert peaked.sum() == 10
+        assert np.allclose(ratio[~peaked], 1.0)
+
+
+def test_fp8_inputs_use_range_and_outliers():
+    w = Workload("f8", 98, 1, 2, 512, 32, "fp8", (False,), outliers=True)
+    a = make_fp8(w)
+    b = make_fp8(w)
+    for name in "qkv":
+        assert a[name].dtype == np.uint8 and a[name].shape == (1, 512, 2, 32)
+        assert a["d" + name].shape == (1, 2) and a["d" + name].dtype == np.float32
+        np.testing.assert_array_equal(a[name], b[name])
+        codes = torch.from_numpy(a[name]).view(torch.float8_e4m3fn).float()
+        assert not torch.isnan(codes).any()
+        # the per-(b,h) amax maps to (close to) the top of the e4m3 range
+        for h in range(2):
+            assert codes[0, :, h, :].abs().max().item() >= 416.0
+        x = dequantize_e4m3(a[name], a["d" + name])
+        # about 0.1% outliers of ~20 sigma
+        assert (np.abs(x) > 8.0).sum() >= 0.0005 * x.size
+
+
+def test_row_sample_includes_ends_and_is_distinct():
+    w = WORKLOADS["long8k"]
+    r = sample_rows(w)
+    assert r.shape == (w.B, w.H, 512)
+    for b in range(w.B):
+        for h in range(w.H):
+            assert r[b, h, 0] == 0 and r[b, h, 1] == w.N - 1
+            assert len(np.unique(r[b, h])) == 512
+            assert r[b, h].min() >= 0 and r[b, h].max() < w.N
+    np.testing.assert_array_equal(r, sample_rows(w))
+    small = sample_rows(WORKLOADS["tiny"])
+    assert small.shape == (1, 2, 128)

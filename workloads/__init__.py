@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for the attention forward.
+
+This module is shared by the tests, the benchmark and the smoke check.  It
+only draws and encodes inputs; it holds none of the attention arithmetic.  The
+CPU oracle and the HIP library both receive exactly the arrays made here
+(the oracle decodes them itself, the library gets device copies).
+
+Workloads (shape B, H, N, d; data; mode):
+  tiny      1, 2, 128, 64      bf16 N(0,1)                      non-causal and causal
+  mha2k     4, 16, 2048, 128   bf16 N(0,1)                      non-causal and causal
+  long8k    2, 16, 8192, 128   bf16 N(0,1)                      causal
+  long8k64  2, 32, 8192, 64    bf16 N(0,1)                      causal
+  ctx32k    1, 32, 32768, 128  bf16 N(0,1), 1% of K rows x8     causal
+  fp8_8k    2, 16, 8192, 128   OCP e4m3 from N(0,1) with 0.1%
+                               outliers x20, per-(b,h) descale  non-causal
+The scale is 1/sqrt(d) everywhere.
+
+Recipe (all draws on the CPU with torch.Generator, so the same seed gives the
+same bytes on every machine running this torch build):
+  * seed = 1000 * workload_id + tensor_id, tensor ids Q=0, K=1, V=2,
+    peaked K rows=3, outlier positions=4 (+ the tensor id * 10), row sample=5;
+  * values: float32 standard normal, laid out [B][N][H][d];
+  * ctx32k: per (b, h), round(0.01 * N) distinct key rows are multiplied by 8
+    in float32 (a peaked softmax that exercises the rescale);
+  * bf16: float32 -> bfloat16 round-to-nearest-even (torch's conversion);
+  * fp8: per tensor, round(0.001 * numel) distinct elements are multiplied by
+    20; then per (b, h): descale = amax / 448 and code = e4m3fn(x / descale)
+    round-to-nearest-even (torch's float8_e4m3fn conversion, after a clamp
+    to +-448 so rounding noise cannot overflow);
+  * sampled rows (large workloads): per (b, h), rows 0 and N-1 plus 510
+    distinct rows drawn uniformly from 1..N-2.
+"""
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str            # "bf16" or "fp8"
+    modes: tuple          # causal flags to run
+    peaked_k: bool = False
+    outliers: bool = False
+
+    @property
+    def scale(self):
+        return 1.0 / math.sqrt(self.d)
+
+    def flops(self, causal):
+        """4*B*H*N^2*d, halved when causal (the metric's convention)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if causal else f
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 1, 2, 128, 64, "bf16", (False, True)),
+    "mha2k": Workload("mha2k", 2, 4, 16, 2048, 128, "bf16", (False, True)),
+    "long8k": Workload("long8k", 3, 2, 16, 8192, 128, "bf16", (True,)),
+    "long8k64": Workload("long8k64", 6, 2, 32, 8192, 64, "bf16", (True,)),
+    "ctx32k": Workload("ctx32k", 4, 1, 32, 32768, 128, "bf16", (True,), peaked_k=True),
+    "fp8_8k": Workload("fp8_8k", 5, 2, 16, 8192, 128, "fp8", (False,), outliers=True),
+}
+
+SAMPLE_ROWS = 512
+E4M3_MAX = 448.0
+
+
+def seed_for(wid, tensor_id):
+    return 1000 * wid + tensor_id
+
+
+def _randn(shape, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def _perm_prefix(n, count, seed):
+    """``count`` distinct integers from range(n), seeded."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    if n <= 1 << 24:
+        return torch.randperm(n, generator=g)[:count]
+    # large n: rejection-free draw of distinct values by oversampling
+    out = torch.empty(0, dtype=torch.int64)
+    while out.numel() < count:
+        cand = torch.randint(0, n, (2 * count,), generator=g)
+        out = torch.unique(torch.cat([out, cand]))  # sorted, distinct
+    # choose a seeded subset of exactly ``count`` of them
+    return out[torch.randperm(out.numel(), generator=g)[:count]]
+
+
+def bf16_bits(t):
+    """float32 torch tensor -> numpy uint16 bit patterns of its bf16 rounding."""
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_bf16(w, shape=None):
+    """Q, K, V for a bf16 workload as uint16 bf16 bit arrays [B][N][H][d]."""
+    B, N, H, d = shape if shape is not None else (w.B, w.N, w.H, w.d)
+    out = {}
+    for tid, name in enumerate(("q", "k", "v")):
+        x = _randn((B, N, H, d), seed_for(w.wid, tid))
+        if name == "k" and w.peaked_k:
+            npk = int(round(0.01 * N))
+            for b in range(B):
+                for h in range(H):
+                    rows = _perm_prefix(N, npk, seed_for(w.wid, 3) * 7919 + b * H + h)
+                    x[b, rows, h, :] *= 8.0
+        out[name] = bf16_bits(x)
+    return out
+
+
+def make_fp8(w, shape=None):
+    """Q, K, V for an fp8 workload: uint8 e4m3fn codes [B][N][H][d] and
+    float32 descales [B][H] per tensor."""
+    B, N, H, d = shape if shape is not None else (w.B, w.N, w.H, w.d)
+    out = {}
+    for tid, name in enumerate(("q", "k", "v")):
+        x = _randn((B, N, H, d), seed_for(w.wid, tid))
+        if w.outliers:
+            n_out = int(round(0.001 * x.numel()))
+            idx = _perm_prefix(x.numel(), n_out, seed_for(w.wid, 4) + 10 * tid)
+            flat = x.view(-1)
+            flat[idx] *= 20.0
+        amax = x.abs().amax(dim=(1, 3))                       # [B][H]
+        descale = torch.clamp(amax, min=1e-30) / E4M3_MAX
+        y = (x / descale[:, None, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
+        out[name] = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        out["d" + name] = descale.to(torch.float32).numpy()
+    return out
+
+
+def make_inputs(w, shape=None):
+    return make_fp8(w, shape) if w.dtype == "fp8" else make_bf16(w, shape)
+
+
+def sample_rows(w, count=SAMPLE_ROWS, N=None):
+    """Per-(b, h) query rows to check: all rows when N <= count, else rows 0
+    and N-1 plus ``count - 2`` distinct seeded rows.  Returns int64 [B][H][R]."""
+    N = w.N if N is None else N
+    if N <= count:
+        return np.broadcast_to(np.arange(N, dtype=np.int64), (w.B, w.H, N)).copy()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(w.wid, 5))
+    rows = np.empty((w.B, w.H, count), dtype=np.int64)
+    for b in range(w.B):
+        for h in range(w.H):
+            mid = torch.randperm(N - 2, generator=g)[:count - 2].numpy() + 1
+            rows[b, h] = np.concatenate([[0, N - 1], np.sort(mid)])
+    return rows
