@@ -1,0 +1,240 @@
+"""Throughput of the tiled exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long8k]
+                    [--no-cpu-baseline] [--copy-calibration]
+
+A step is one pass of the whole hot path -- one attn_fwd (or attn_fwd_fp8)
+launch: Q/K/V tile loads, both MFMA products, the online softmax with its
+gated rescale, causal masking, and the O/LSE epilogue -- over one batch of
+seeded synthetic inputs already resident in HBM.  W untimed steps, then K
+steps timed with HIP events on the stream the kernel is launched on (torch's
+current stream).  Prints ONE JSON line.
+
+Default workload long8k: B=2, H=16, N=8192, d=128, bf16, causal, scale
+1/sqrt(d) -- the first bf16 workload at the N >= 8192, d = 128 size the
+throughput target is stated for.  Other workloads (--workload) are for
+exploration; the parity tests cover all of them.
+
+TFLOPS = 4*B*H*N^2*d (halved when causal) / time per step.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz dense MFMA
+METRIC = "attn fwd TFLOPS (4BHN²d, causal halved) + % of MI355X MFMA peak, 1 GPU"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_attention_tile_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, causal):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    key = "%s_%s" % (workload, "causal" if causal else "noncausal")
+    ent = rec.get(key)
+    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def _one_head(w, inp, causal, b, h, rows):
+    from oracle import attention_head_rows, bf16_bits_to_float64, dequantize_e4m3
+    if w.dtype == "fp8":
+        def deq(name):
+            return dequantize_e4m3(inp[name][b:b + 1, :, h:h + 1, :],
+                                   inp["d" + name][b:b + 1, h:h + 1])[0, :, 0, :]
+        q, k, v = deq("q"), deq("k"), deq("v")
+    else:
+        q = bf16_bits_to_float64(inp["q"][b, :, h, :])
+        k = bf16_bits_to_float64(inp["k"][b, :, h, :])
+        v = bf16_bits_to_float64(inp["v"][b, :, h, :])
+    return attention_head_rows(q, k, v, w.scale, causal, rows)
+
+
+def cpu_baseline(w, inp, causal, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    seeded query rows of the workload's heads, as many as fit in about
+    ``budget_s`` seconds (a first pass of 512 rows per head sizes the
+    sample)."""
+    import numpy as np
+    from workloads import sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    # size the sample: time 512 rows of the first head, then pick the row
+    # count per head that fills the budget over all heads
+    probe = sample_rows(w, count=min(512, w.N))
+    t0 = time.perf_counter()
+    _one_head(w, inp, causal, 0, 0, probe[0, 0])
+    per_row = (time.perf_counter() - t0) / probe.shape[2]
+    count = int(min(w.N, max(512, budget_s / max(per_row, 1e-9) / len(heads))))
+    rows = sample_rows(w, count=count)
+    flops = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        r = rows[b, h]
+        _one_head(w, inp, causal, b, h, r)
+        vis = (r + 1) if causal else np.full(r.shape, w.N)
+        flops += float(4.0 * w.d * vis.sum())
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": "fp64 NumPy oracle on %d seeded query rows of each of %d/%d heads "
+                  "(%.2f GFLOP counted with the metric's 4*d*visible_keys per row, %.1f s)"
+                  % (rows.shape[2], done, len(heads), flops / 1e9, dt),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long8k")
+    ap.add_argument("--causal", type=int, default=None, help="override the workload's mode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the work shards by (batch, head) with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import exact_attention_tile_amd as eat
+    from workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    eat.load_library()
+    w = WORKLOADS[args.workload]
+    causal = bool(w.modes[0] if args.causal is None else args.causal)
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if w.dtype == "fp8":
+        q = torch.from_numpy(inp["q"]).to(dev)
+        k = torch.from_numpy(inp["k"]).to(dev)
+        v = torch.from_numpy(inp["v"]).to(dev)
+        dq = torch.from_numpy(inp["dq"]).reshape(-1).to(dev)
+        dk = torch.from_numpy(inp["dk"]).reshape(-1).to(dev)
+        dv = torch.from_numpy(inp["dv"]).reshape(-1).to(dev)
+
+        def step():
+            eat.attn_fwd_fp8(q, k, v, o, lse, dq, dk, dv, w.B, w.H, w.N, w.d, int(causal),
+                             w.scale, stream)
+    else:
+        def dev16(x):
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        q, k, v = dev16(inp["q"]), dev16(inp["k"]), dev16(inp["v"])
+
+        def step():
+            eat.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(causal), w.scale, stream)
+
+    o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    if not bool(torch.isfinite(lse).all()) or not bool(torch.isfinite(o.float()).all()):
+        print("non-finite output", file=sys.stderr)
+        sys.exit(1)
+
+    flops = w.flops(causal)
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, workloads/)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": causal, "scale": w.scale,
+                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(w.name, causal),
+                     "kernel_avg_ms": round(avg_launch_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, causal)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

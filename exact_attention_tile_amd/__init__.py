@@ -1,0 +1,17 @@
+"""MI355X (gfx950) tiled exact attention forward.
+
+A thin ctypes binding over the C ABI declared in ``include/attn.h``
+(``libattn.so``, built in-tree by ``exact_attention_tile_amd.build``).  Every
+step of the attention runs in the library's HIP kernels; this module only
+marshals arguments.  There is no CPU fallback: without the built library the
+import of the binding raises.
+"""
+
+from ._binding import (ATTN_ERR_HIP, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_OK,
+                       AttnError, attn_fwd, attn_fwd_fp8, attn_status_string, attn_version,
+                       lib_path, load_library)
+
+__all__ = [
+    "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "AttnError",
+    "attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_version", "lib_path", "load_library",
+]

@@ -1,0 +1,103 @@
+"""ctypes marshalling for libattn.so (C ABI in include/attn.h).
+
+Pointer arguments accept a plain integer device address or any object with a
+``data_ptr()`` method (a torch tensor); ``stream`` accepts an integer HIP
+stream handle, ``None``/0 (the null stream) or an object with a
+``cuda_stream`` attribute (a torch stream).
+"""
+
+import ctypes
+import os
+
+ATTN_OK = 0
+ATTN_ERR_INVALID_ARG = 1
+ATTN_ERR_UNSUPPORTED = 2
+ATTN_ERR_HIP = 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path():
+    return os.path.join(_HERE, "libattn.so")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s returned %d (%s)" % (where, status, attn_status_string(status)))
+
+
+def load_library():
+    """Loads the in-tree libattn.so once; raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    try:
+        # share torch's HIP runtime (same SONAME) so its streams and device
+        # pointers are valid in the library's calls
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise RuntimeError("libattn.so is not built (%s); run "
+                           "`python -m exact_attention_tile_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_fwd_fp8.restype = i
+    lib.attn_status_string.argtypes = [i]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        return None
+    if isinstance(s, int):
+        return s or None
+    return s.cuda_stream or None
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_version():
+    return load_library().attn_version().decode()
+
+
+def attn_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None, check=True):
+    """bf16 forward; see attn_fwd in include/attn.h.  Returns the status;
+    raises AttnError on a non-zero status when ``check``."""
+    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                 int(N), int(d), int(causal), float(scale), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+    return st
+
+
+def attn_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, N, d, causal, scale,
+                 stream=None, check=True):
+    """OCP e4m3 forward; see attn_fwd_fp8 in include/attn.h."""
+    st = load_library().attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     _ptr(descale_q), _ptr(descale_k), _ptr(descale_v), int(B),
+                                     int(H), int(N), int(d), int(causal), float(scale),
+                                     _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8")
+    return st

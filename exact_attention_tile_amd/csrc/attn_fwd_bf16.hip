@@ -1,0 +1,333 @@
+// bf16 tiled exact attention forward for gfx950 (MI355X, CDNA4).
+//
+// What it computes: O = softmax(Q K^T * scale) V and lse = ln sum exp(scores)
+// per query row, on [B][N][H][d] tensors ("FlashAttention-4 no Blackwell
+// B200 ...", section "Por que o Blackwell exige mais do que multiplicações
+// rápidas"), tile by tile with an online softmax so the N x N scores stay on
+// chip (dev.to "FlashAttention-4 em Blackwell B200", sections 1 and 4), with
+// the threshold-gated rescale of "FlashAttention 4: Atenção Mais Rápida ...",
+// section "Reescalonamento Softmax Online Mais Inteligente".
+//
+// Work decomposition
+//   one work-group = NW waves = 32*NW query rows of one (batch, head);
+//   one wave       = 32 query rows, for which it owns the output tile;
+//   K/V tiles of BC keys are streamed HBM -> registers -> LDS, double
+//   buffered: tile j+1 is fetched while tile j is computed, one barrier per
+//   tile.
+//
+// Transposed formulation.  Each wave computes S^T = K_j Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T kept in VGPRs for
+// the whole kernel).  In the 32x32 accumulator layout lane l holds column
+// l%32 -- one query -- and 16 of the 32 key rows (row 8*(r/4)+4*(l/32)+r%4 for
+// register r).  So the row max and row sum of the softmax are in-lane
+// reductions plus one exchange with lane l^32 (permlane32_swap), the rescale
+// factor is a per-lane scalar on that lane's output registers, and the
+// exponentials, converted to bf16, are already in the B-operand layout of the
+// second product O^T += V_j^T P^T: B slot t of lane-half h holds key
+// pi(h,t) = 4h + (t&3) + 8*(t>>2) of a 16-key group.  The matching A operand
+// (V^T, 8 keys x 1 column per lane) comes straight from the row-major V tile
+// with two ds_read_b64_tr_b16 (transposing LDS reads of 4 rows x 16 columns
+// per 16-lane group).
+//
+// Softmax in base 2: scores are kept as s*c with c = |scale|*log2(e) folded
+// into one fma; p = exp2(s*c - m_ref) on v_exp_f32.  m_ref only moves when a
+// tile's row maximum exceeds it by more than TAU (log2 units), so p <= 2^TAU
+// and most tiles skip the O rescale; the skip is decided per wave (ballot).
+#include "attn_kernels.hpp"
+
+namespace attn {
+
+constexpr float kTauBf16 = 8.0f;  // p <= 256: exact range for bf16 / fp32
+
+// 16-byte-chunk XOR swizzles of the row-major [BC][D] LDS tiles.
+//  K: a ds_read_b128 A-operand read has 16 lanes on 16 consecutive rows at
+//     one chunk -> the swizzle spreads them over all 64 banks.
+//  V: a ds_read_b64_tr_b16 read has each 32 lanes on 4 consecutive rows x 4
+//     consecutive chunks -> the swizzle moves each row's 64 bytes to a
+//     distinct quarter of the bank space.
+template <int D> __device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+template <int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(BC % 32 == 0, "kv tile");
+  constexpr int T = NW * 64;             // threads
+  constexpr int BR = NW * 32;            // query rows per work-group
+  constexpr int CPR = D / 8;             // 16-byte chunks per row
+  constexpr int CPT = BC * CPR / T;      // chunks per thread per tensor per tile
+  static_assert(CPT * T == BC * CPR, "tile must split evenly over threads");
+  constexpr int NKB = BC / 32;           // 32-key blocks per tile
+  constexpr int NDB = D / 32;            // 32-wide column blocks of the output
+  constexpr int NKS = D / 16;            // k-steps of the QK^T product
+
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * BC * D];
+  __bf16* ks_base = smem;                // [2][BC][D]
+  __bf16* vs_base = smem + 2 * BC * D;   // [2][BC][D]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+
+  int bh, qt;
+  block_to_work(p, bh, qt);
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int N = p.N;
+  const long long tok = (long long)p.H * D;                       // elements between tokens
+  const long long head_base = ((long long)b * N * p.H + h) * D;   // element (b, 0, h, 0)
+
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wave * 32;
+  const int myq = qw0 + ln;
+
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
+
+  // ---- Q^T fragments (B operand): lane (n=ln, h=lh) holds Q[myq][16ks+8lh .. +7]
+  bf16x8 qf[NKS];
+  {
+    const int qr = myq < N ? myq : N - 1;
+    const u32x4* src = (const u32x4*)(qg + (long long)qr * tok + 8 * lh);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 t = src[2 * ks];
+      t ^= p.qsign;
+      qf[ks] = __builtin_bit_cast(bf16x8, t);
+    }
+  }
+
+  // ---- tile range of this work-group and of this wave
+  const int n_kv_all = (N + BC - 1) / BC;
+  int wg_tiles = n_kv_all;
+  int wv_tiles = qw0 < N ? n_kv_all : 0;
+  if (CAUSAL) {
+    const int last_wg = min(q0 + BR - 1, N - 1);
+    wg_tiles = last_wg / BC + 1;
+    if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
+  }
+
+  // ---- cooperative K/V tile loader (global -> registers -> swizzled LDS)
+  u32x4 kreg[CPT], vreg[CPT];
+  auto fetch = [&](int j) {
+    const int kv0 = j * BC;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * T;
+      const int row = c / CPR;
+      const int col = c - row * CPR;
+      const int n = kv0 + row;
+      if (n < N) {
+        const long long off = (long long)n * tok + col * 8;
+        kreg[i] = *(const u32x4*)(kg + off);
+        vreg[i] = *(const u32x4*)(vg + off);
+      } else {
+        kreg[i] = u32x4{0u, 0u, 0u, 0u};
+        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+    __bf16* kd = ks_base + buf * BC * D;
+    __bf16* vd = vs_base + buf * BC * D;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * T;
+      const int row = c / CPR;
+      const int col = c - row * CPR;
+      *(u32x4*)(kd + row * D + ((col ^ swz_k<D>(row)) * 8)) = kreg[i];
+      *(u32x4*)(vd + row * D + ((col ^ swz_v<D>(row)) * 8)) = vreg[i];
+    }
+  };
+
+  // ---- per-lane LDS read offsets (elements), hoisted out of the loop
+  // K A-operand: row kb*32+ln, chunk 2ks+lh (swizzled by the row)
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = ln * D + (((2 * ks + lh) ^ swz_k<D>(ln)) * 8);
+  // V^T A-operand via the transposing read: in each 16-lane group, source
+  // lane i reads row key0 + i/4, columns d0 + 4*(i%4) .. +3.
+  const int gi = lane & 15;
+  const int vrow_l = 4 * lh + (gi >> 2);                  // row within a 16-key group (half 0)
+  const int vsw = swz_v<D>(vrow_l);                        // rows differ by multiples of 4 -> constant
+  int voff[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int chunk = 4 * db + ((lane & 16) >> 3) + ((gi & 3) >> 1);
+    voff[db] = vrow_l * D + ((chunk ^ vsw) * 8) + (gi & 1) * 4;
+  }
+
+  // ---- running state
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  float m_ref = -__builtin_inff();   // reference max, log2 units
+  float l_part = 0.f;                // this lane-half's share of the row sum
+  const float c = p.c;
+
+  if (wg_tiles > 0) {
+    fetch(0);
+    stash(0);
+  }
+  __syncthreads();
+
+  for (int j = 0; j < wg_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < wg_tiles) fetch(j + 1);
+
+    if (j < wv_tiles) {
+      const __bf16* kt = ks_base + buf * BC * D;
+      const __bf16* vt = vs_base + buf * BC * D;
+      const int kv0 = j * BC;
+
+      // S^T = K_j Q^T
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          bf16x8 a = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+        }
+      }
+
+      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+      unsigned long long vis = ~0ull;   // bit kb*16 + r: key visible
+      float mx = -__builtin_inff();
+      if (masked) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const bool ok = key < N && (!CAUSAL || key <= myq);
+            if (!ok) vis &= ~(1ull << (kb * 16 + r));
+            mx = fmaxf(mx, ok ? s[kb][r] : -__builtin_inff());
+          }
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      }
+      mx = pair_max(mx);
+
+      // threshold-gated rescale (decided per lane, skipped per wave)
+      const float mt = mx * c;
+      const bool need = mt > m_ref + kTauBf16;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
+        m_ref = need ? mt : m_ref;
+        l_part *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+
+      // exponentials, row-sum share, bf16 probabilities in B-operand order
+      const float neg_m = -m_ref;
+      bf16x8 pf[BC / 16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float e[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int r = half * 8 + t;
+            float x = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+            if (masked) x = ((vis >> (kb * 16 + r)) & 1ull) ? x : 0.f;
+            e[t] = x;
+            l_part += x;
+          }
+          u32x4 w;
+          w[0] = pack_bf16x2(e[0], e[1]);
+          w[1] = pack_bf16x2(e[2], e[3]);
+          w[2] = pack_bf16x2(e[4], e[5]);
+          w[3] = pack_bf16x2(e[6], e[7]);
+          pf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
+
+      // O^T += V_j^T P^T
+#pragma unroll
+      for (int kk = 0; kk < BC / 16; ++kk) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const __bf16* vb = vt + kk * 16 * D + voff[db];
+          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb));
+          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb + 8 * D));
+          i32x4 w;
+          w[0] = (int)(unsigned short)lo[0] | ((int)(unsigned short)lo[1] << 16);
+          w[1] = (int)(unsigned short)lo[2] | ((int)(unsigned short)lo[3] << 16);
+          w[2] = (int)(unsigned short)hi[0] | ((int)(unsigned short)hi[1] << 16);
+          w[3] = (int)(unsigned short)hi[2] | ((int)(unsigned short)hi[3] << 16);
+          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kk],
+                                                            oacc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (j + 1 < wg_tiles) stash(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = acc / l -> bf16, lse = ln2 * (m_ref + log2 l)
+  const float l_tot = pair_sum(l_part);   // wave-uniform exchange, before any lane test
+  if (myq < N) {
+    const float inv = 1.f / l_tot;
+    __bf16* og = (__bf16*)p.o + head_base + (long long)myq * tok;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = db * 32 + 8 * g + 4 * lh;
+        u32x2 w;
+        w[0] = pack_bf16x2(oacc[db][4 * g + 0] * inv, oacc[db][4 * g + 1] * inv);
+        w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
+        *(u32x2*)(og + d0) = w;
+      }
+    }
+    if (lh == 0) {
+      p.lse[(long long)bh * N + myq] = (m_ref + fast_log2(l_tot)) * 0.69314718055994531f;
+    }
+  }
+}
+
+}  // namespace attn
+
+// ---------------------------------------------------------------------------
+// host-side launch helpers (called by the C ABI in attn_api.cpp)
+// ---------------------------------------------------------------------------
+namespace attn {
+
+template <int D, int NW, int BC, bool CAUSAL>
+static hipError_t launch_bf16_t(const FwdParams& prm, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BC, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream,
+                     prm);
+  return hipGetLastError();
+}
+
+// Rows per work-group for each head dim (queries = 32 per wave).
+int bf16_rows_per_block(int d) { return d == 128 ? 8 * 32 : 8 * 32; }
+
+hipError_t launch_bf16(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream) {
+  if (d == 128) {
+    return causal ? launch_bf16_t<128, 8, 64, true>(prm, grid, stream)
+                  : launch_bf16_t<128, 8, 64, false>(prm, grid, stream);
+  }
+  return causal ? launch_bf16_t<64, 8, 64, true>(prm, grid, stream)
+                : launch_bf16_t<64, 8, 64, false>(prm, grid, stream);
+}
+
+}  // namespace attn

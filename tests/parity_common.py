@@ -1,0 +1,143 @@
+"""Helpers for the GPU parity tests: run the HIP library through its C ABI
+on seeded inputs and compare with the CPU oracle.
+
+Tolerances (fixed by the method's accuracy target):
+  bf16 : O max-abs <= 2e-2, O relative RMS <= 5e-3, LSE max-abs <= 1e-3
+  fp8  : O relative RMS <= 3e-2, LSE max-abs <= 1e-3
+relative RMS = ||O_gpu - O_ref||_2 / ||O_ref||_2 over every checked element.
+"""
+
+import numpy as np
+import torch
+
+import exact_attention_tile_amd as eat
+from oracle import attention_forward, bf16_bits_to_float64, dequantize_e4m3
+
+BF16_MAXABS = 2e-2
+BF16_RELRMS = 5e-3
+LSE_MAXABS = 1e-3
+FP8_RELRMS = 3e-2
+
+GUARD = 4096          # sentinel elements on each side of O and LSE
+SENTINEL_BF16 = 0x7FC1  # a NaN pattern the kernel never writes
+SENTINEL_F32 = 0x7FC00001
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU test run without a visible GPU")
+    eat.load_library()
+
+
+def dev_u16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_u8(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).cuda()
+
+
+class Guarded:
+    """O (bf16) and LSE (fp32) buffers with sentinel-filled margins."""
+
+    def __init__(self, B, N, H, d):
+        self.no = B * N * H * d
+        self.nl = B * H * N
+        self.o_raw = torch.full((self.no + 2 * GUARD,), SENTINEL_BF16, dtype=torch.int16,
+                                device="cuda")
+        self.l_raw = torch.full((self.nl + 2 * GUARD,), SENTINEL_F32, dtype=torch.int32,
+                                device="cuda")
+        self.shape = (B, N, H, d)
+        self.lshape = (B, H, N)
+
+    @property
+    def o_ptr(self):
+        return self.o_raw.data_ptr() + 2 * GUARD
+
+    @property
+    def l_ptr(self):
+        return self.l_raw.data_ptr() + 4 * GUARD
+
+    def o(self):
+        return self.o_raw[GUARD:GUARD + self.no].view(torch.bfloat16).view(self.shape)
+
+    def lse(self):
+        return self.l_raw[GUARD:GUARD + self.nl].view(torch.float32).view(self.lshape)
+
+    def guards_intact(self):
+        o_ok = bool((self.o_raw[:GUARD] == SENTINEL_BF16).all() and
+                    (self.o_raw[GUARD + self.no:] == SENTINEL_BF16).all())
+        l_ok = bool((self.l_raw[:GUARD] == SENTINEL_F32).all() and
+                    (self.l_raw[GUARD + self.nl:] == SENTINEL_F32).all())
+        return o_ok and l_ok
+
+
+def run_bf16(inp, B, H, N, d, causal, scale):
+    q, k, v = dev_u16(inp["q"]), dev_u16(inp["k"]), dev_u16(inp["v"])
+    out = Guarded(B, N, H, d)
+    eat.attn_fwd(q, k, v, out.o_ptr, out.l_ptr, B, H, N, d, int(causal), scale,
+                 torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return out
+
+
+def run_fp8(inp, B, H, N, d, causal, scale):
+    q, k, v = dev_u8(inp["q"]), dev_u8(inp["k"]), dev_u8(inp["v"])
+    dq = torch.from_numpy(inp["dq"]).reshape(-1).cuda()
+    dk = torch.from_numpy(inp["dk"]).reshape(-1).cuda()
+    dv = torch.from_numpy(inp["dv"]).reshape(-1).cuda()
+    out = Guarded(B, N, H, d)
+    eat.attn_fwd_fp8(q, k, v, out.o_ptr, out.l_ptr, dq, dk, dv, B, H, N, d, int(causal), scale,
+                     torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    return out
+
+
+def reference(inp, dtype, causal, scale, rows=None):
+    if dtype == "fp8":
+        q = dequantize_e4m3(inp["q"], inp["dq"])
+        k = dequantize_e4m3(inp["k"], inp["dk"])
+        v = dequantize_e4m3(inp["v"], inp["dv"])
+    else:
+        q = bf16_bits_to_float64(inp["q"])
+        k = bf16_bits_to_float64(inp["k"])
+        v = bf16_bits_to_float64(inp["v"])
+    return attention_forward(q, k, v, scale, causal, rows=rows)
+
+
+def errors(out, ref_o, ref_lse, rows=None):
+    """Returns (max_abs_O, rel_rms_O, max_abs_LSE) on the checked rows."""
+    o = out.o().float().cpu().numpy().astype(np.float64)      # [B][N][H][d]
+    lse = out.lse().cpu().numpy().astype(np.float64)          # [B][H][N]
+    if rows is None:
+        go, gl = o, lse
+    else:
+        B, H, R = rows.shape
+        go = np.empty(ref_o.shape)
+        gl = np.empty(ref_lse.shape)
+        for b in range(B):
+            for h in range(H):
+                go[b, h] = o[b, rows[b, h], h, :]
+                gl[b, h] = lse[b, h, rows[b, h]]
+    diff = go - ref_o
+    max_abs = float(np.abs(diff).max())
+    rel_rms = float(np.sqrt((diff ** 2).sum() / (ref_o ** 2).sum()))
+    lse_abs = float(np.abs(gl - ref_lse).max())
+    return max_abs, rel_rms, lse_abs
+
+
+def assert_bf16_ok(err, label):
+    max_abs, rel_rms, lse_abs = err
+    msg = "%s: max_abs=%.3e rel_rms=%.3e lse=%.3e" % (label, max_abs, rel_rms, lse_abs)
+    print(msg, flush=True)
+    assert max_abs <= BF16_MAXABS, msg
+    assert rel_rms <= BF16_RELRMS, msg
+    assert lse_abs <= LSE_MAXABS, msg
+
+
+def assert_fp8_ok(err, label):
+    max_abs, rel_rms, lse_abs = err
+    msg = "%s: max_abs=%.3e rel_rms=%.3e lse=%.3e" % (label, max_abs, rel_rms, lse_abs)
+    print(msg, flush=True)
+    assert rel_rms <= FP8_RELRMS, msg
+    assert lse_abs <= LSE_MAXABS, msg

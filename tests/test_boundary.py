@@ -1,0 +1,109 @@
+"""The C-ABI library: it loads, exports every function include/attn.h
+declares, and rejects invalid arguments on the host (before any HIP call, so
+these run without a GPU)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import exact_attention_tile_amd as eat
+from exact_attention_tile_amd import build as eat_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(eat.lib_path()):
+        eat_build.build()
+    return eat.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == {"attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_version"}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert isinstance(getattr(lib, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(lib):
+    assert eat.attn_status_string(eat.ATTN_OK) == "ATTN_OK"
+    assert eat.attn_status_string(eat.ATTN_ERR_INVALID_ARG) == "ATTN_ERR_INVALID_ARG"
+    assert eat.attn_status_string(eat.ATTN_ERR_UNSUPPORTED) == "ATTN_ERR_UNSUPPORTED"
+    assert eat.attn_status_string(eat.ATTN_ERR_HIP) == "ATTN_ERR_HIP"
+    assert eat.attn_status_string(42) == "ATTN_ERR_UNKNOWN"
+    assert "gfx950" in eat.attn_version()
+
+
+# Fake, 16-byte-aligned, never-dereferenced "device" addresses: every case
+# below must be rejected by host-side validation before anything touches
+# them.
+P = 0x10000
+GOOD = dict(q=P, k=P + 0x1000, v=P + 0x2000, o=P + 0x3000, lse=P + 0x4000,
+            B=1, H=2, N=128, d=64, causal=0, scale=0.125)
+
+
+def call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return eat.attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                        a["causal"], a["scale"], None, check=False)
+
+
+def call8(**kw):
+    a = dict(GOOD, dq=P + 0x5000, dk=P + 0x5100, dv=P + 0x5200)
+    a.update(kw)
+    return eat.attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"], a["dv"],
+                            a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], None,
+                            check=False)
+
+
+@pytest.mark.parametrize("fn", [call, call8])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(k=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(v=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(o=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(lse=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(H=-1), eat.ATTN_ERR_INVALID_ARG),
+    (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(causal=2), eat.ATTN_ERR_INVALID_ARG),
+    (dict(causal=-1), eat.ATTN_ERR_INVALID_ARG),
+    (dict(scale=math.inf), eat.ATTN_ERR_INVALID_ARG),
+    (dict(scale=math.nan), eat.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(d=256), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(d=0), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(q=P + 8), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(o=P + 0x3002), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(lse=P + 0x4002), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(B=1 << 30, N=1 << 30, H=1 << 30), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=65535, H=65535, N=1 << 20), eat.ATTN_ERR_UNSUPPORTED),   # grid beyond 2^31 blocks
+])
+def test_invalid_arguments_rejected_on_host(lib, fn, kw, status):
+    assert fn(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(dq=0), dict(dk=0), dict(dv=0)])
+def test_fp8_requires_descales(lib, kw):
+    assert call8(**kw) == eat.ATTN_ERR_INVALID_ARG
+
+
+def test_binding_raises_with_status_name(lib):
+    with pytest.raises(eat.AttnError, match="ATTN_ERR_UNSUPPORTED"):
+        eat.attn_fwd(P, P, P, P, P, 1, 1, 16, 80, 0, 1.0)
