@@ -57,7 +57,9 @@ int plan(attn::FwdParams& prm, int rows_per_block, int* grid_out) {
 }
 
 void set_scale(attn::FwdParams& prm, float scale, unsigned neg_mask) {
-  prm.c = fabsf(scale) * 1.4426950408889634f;
+  // kernels mask scores with -inf before the fma(s, c, -m): c must be > 0.
+  // For |scale| this small every s*c rounds to 0 either way.
+  prm.c = fmaxf(fabsf(scale) * 1.4426950408889634f, 1e-30f);
   prm.qsign = scale < 0.f ? neg_mask : 0u;
 }
 

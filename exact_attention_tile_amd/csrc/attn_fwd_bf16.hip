@@ -11,9 +11,8 @@
 // Work decomposition
 //   one work-group = NW waves = 32*NW query rows of one (batch, head);
 //   one wave       = 32 query rows, for which it owns the output tile;
-//   K/V tiles of BC keys are streamed HBM -> registers -> LDS, double
-//   buffered: tile j+1 is fetched while tile j is computed, one barrier per
-//   tile.
+//   K/V tiles of BC keys are streamed HBM -> LDS (global_load_lds, no
+//   registers), double buffered, one barrier per tile.
 //
 // Transposed formulation.  Each wave computes S^T = K_j Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T kept in VGPRs for
@@ -29,10 +28,20 @@
 // with two ds_read_b64_tr_b16 (transposing LDS reads of 4 rows x 16 columns
 // per 16-lane group).
 //
+// Overlap inside a wave (software pipeline).  K runs one tile ahead of V: in
+// step j a wave issues the S^T product of tile j+1 on the matrix cores and,
+// interleaved with those MFMAs in its instruction stream, the exponentials of
+// tile j on the vector ALU; then the P.V product of tile j.  Two waves share
+// each SIMD and fill each other's gaps.
+//
 // Softmax in base 2: scores are kept as s*c with c = |scale|*log2(e) folded
 // into one fma; p = exp2(s*c - m_ref) on v_exp_f32.  m_ref only moves when a
 // tile's row maximum exceeds it by more than TAU (log2 units), so p <= 2^TAU
 // and most tiles skip the O rescale; the skip is decided per wave (ballot).
+// The row sum adds the fp32 p (rounding p to bf16 first would cost the
+// log-sum-exp up to 2^-9 relative in l).
+#include <type_traits>
+
 #include "attn_kernels.hpp"
 
 namespace attn {
@@ -52,10 +61,15 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// sched_group_barrier masks
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
+
 template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(BC % 32 == 0, "kv tile");
+  static_assert(BC == 64, "kv tile");
   constexpr int T = NW * 64;             // threads
   constexpr int BR = NW * 32;            // query rows per work-group
   constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -64,10 +78,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   constexpr int NKB = BC / 32;           // 32-key blocks per tile
   constexpr int NDB = D / 32;            // 32-wide column blocks of the output
   constexpr int NKS = D / 16;            // k-steps of the QK^T product
+  constexpr int NKK = BC / 16;           // 16-key steps of the P.V product
 
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * BC * D];
-  __bf16* ks_base = smem;                // [2][BC][D]
-  __bf16* vs_base = smem + 2 * BC * D;   // [2][BC][D]
+  __bf16* ks_base = smem;                // K tiles: [2][BC][D]
+  __bf16* vs_base = smem + 2 * BC * D;   // V tiles: [2][BC][D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -114,40 +129,42 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
   }
 
-  // ---- cooperative K/V tile loader (global -> registers -> swizzled LDS)
-  u32x4 kreg[CPT], vreg[CPT];
-  auto fetch = [&](int j) {
+  // ---- tile loader: global_load_lds_dwordx4 straight into the swizzled LDS
+  // tile.  One instruction fills 1 KiB of LDS, lane l writing bytes
+  // [16 l, 16 l + 16) after the wave-uniform base; so the swizzle is applied
+  // by choosing each lane's source chunk.  Rows past N are clamped to row
+  // N-1: their keys are masked, so they contribute p = 0 against finite V.
+  constexpr int LPW = BC * D * 2 / 1024 / NW;          // loads per wave per tensor per tile
+  static_assert(LPW * 1024 * NW == BC * D * 2, "tile must split into 1 KiB per wave");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  int ld_row[LPW], ld_kcol[LPW], ld_vcol[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int off = (wave * LPW + i) * 512 + lane * 8;   // element offset in the tile
+    const int row = off / D;
+    const int pc = (off - row * D) / 8;                   // physical 16-byte chunk
+    ld_row[i] = row;
+    ld_kcol[i] = (pc ^ swz_k<D>(row)) * 8;
+    ld_vcol[i] = (pc ^ swz_v<D>(row)) * 8;
+  }
+  auto load_tile = [&](const __bf16* src, const int* col, __bf16* dst_tile, int j) {
     const int kv0 = j * BC;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * T;
-      const int row = c / CPR;
-      const int col = c - row * CPR;
-      const int n = kv0 + row;
-      if (n < N) {
-        const long long off = (long long)n * tok + col * 8;
-        kreg[i] = *(const u32x4*)(kg + off);
-        vreg[i] = *(const u32x4*)(vg + off);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < LPW; ++i) {
+      const int n = min(kv0 + ld_row[i], N - 1);
+      const __bf16* g = src + (long long)n * tok + col[i];
+      __bf16* l = dst_tile + (wave_u * LPW + i) * 512;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (ATTN_LDS void*)l, 16, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-    __bf16* kd = ks_base + buf * BC * D;
-    __bf16* vd = vs_base + buf * BC * D;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * T;
-      const int row = c / CPR;
-      const int col = c - row * CPR;
-      *(u32x4*)(kd + row * D + ((col ^ swz_k<D>(row)) * 8)) = kreg[i];
-      *(u32x4*)(vd + row * D + ((col ^ swz_v<D>(row)) * 8)) = vreg[i];
-    }
-  };
+  auto load_k = [&](int j, int buf) { load_tile(kg, ld_kcol, ks_base + buf * BC * D, j); };
+  auto load_v = [&](int j, int buf) { load_tile(vg, ld_vcol, vs_base + buf * BC * D, j); };
+  // vmcnt(0): this wave's LDS-bound loads have landed (before the barrier
+  // that publishes them)
+  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
-  // ---- per-lane LDS read offsets (elements), hoisted out of the loop
+  // ---- per-lane LDS read offsets (elements)
   // K A-operand: row kb*32+ln, chunk 2ks+lh (swizzled by the row)
   int koff[NKS];
 #pragma unroll
@@ -169,99 +186,102 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_ref = -__builtin_inff();   // reference max, log2 units
-  float l_part = 0.f;                // this lane-half's share of the row sum
+  float l_part[2] = {0.f, 0.f};      // this lane-half's share of the row sum (2 chains)
   const float c = p.c;
-
-  if (wg_tiles > 0) {
-    fetch(0);
-    stash(0);
+  f32x16 s_cur[NKB];                 // S^T of the tile being finished
+  f32x16 s_nxt[NKB];                 // S^T of the next tile (in flight)
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s_cur[kb] = f32x16{};
+    s_nxt[kb] = f32x16{};
   }
-  __syncthreads();
 
-  for (int j = 0; j < wg_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < wg_tiles) fetch(j + 1);
+  // ---- pieces of one pipeline step ----------------------------------------
+  // row max of s_cur (with the mask when MASKED) and the gated rescale of
+  // m_ref / l_part / oacc
+  auto stats = [&](auto masked_tag, int kv0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
+      // off - 4*lh <= lim
+      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s_cur[kb][r] = -__builtin_inff();
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s_cur[kb][r]), s_cur[kb][r + 1]);
+    mx = pair_max(mx);
+    const float mt = mx * c;
+    const bool need = mt > m_ref + kTauBf16;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
+      m_ref = need ? mt : m_ref;
+      l_part[0] *= alpha;
+      l_part[1] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+  };
 
-    if (j < wv_tiles) {
-      const __bf16* kt = ks_base + buf * BC * D;
-      const __bf16* vt = vs_base + buf * BC * D;
-      const int kv0 = j * BC;
-
-      // S^T = K_j Q^T
-      f32x16 s[NKB];
+  // S^T of the next tile (K buffer kt) into s_nxt, interleaved with the
+  // exponentials of s_cur (when HAS_CUR); then, when HAS_CUR,
+  // O^T += V^T P^T from V buffer vt.
+  auto step = [&](auto cur_tag, auto nxt_tag, const __bf16* kt, const __bf16* vt) {
+    constexpr bool HAS_CUR = decltype(cur_tag)::value;
+    constexpr bool HAS_NXT = decltype(nxt_tag)::value;
+    bf16x8 pf[NKK];
+    if constexpr (HAS_NXT) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
+        s_nxt[kb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
           bf16x8 a = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+          s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s_nxt[kb], 0, 0, 0);
         }
       }
-
-      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-      unsigned long long vis = ~0ull;   // bit kb*16 + r: key visible
-      float mx = -__builtin_inff();
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= myq);
-            if (!ok) vis &= ~(1ull << (kb * 16 + r));
-            mx = fmaxf(mx, ok ? s[kb][r] : -__builtin_inff());
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      }
-      mx = pair_max(mx);
-
-      // threshold-gated rescale (decided per lane, skipped per wave)
-      const float mt = mx * c;
-      const bool need = mt > m_ref + kTauBf16;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
-        m_ref = need ? mt : m_ref;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-
-      // exponentials, row-sum share, bf16 probabilities in B-operand order
+    }
+    if constexpr (HAS_CUR) {
       const float neg_m = -m_ref;
-      bf16x8 pf[BC / 16];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          float e[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const int r = half * 8 + t;
-            float x = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
-            if (masked) x = ((vis >> (kb * 16 + r)) & 1ull) ? x : 0.f;
-            e[t] = x;
-            l_part += x;
-          }
           u32x4 w;
-          w[0] = pack_bf16x2(e[0], e[1]);
-          w[1] = pack_bf16x2(e[2], e[3]);
-          w[2] = pack_bf16x2(e[4], e[5]);
-          w[3] = pack_bf16x2(e[6], e[7]);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = half * 8 + 2 * t;
+            const float e0 = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
+            const float e1 = fast_exp2(__builtin_fmaf(s_cur[kb][r + 1], c, neg_m));
+            w[t] = pack_bf16x2(e0, e1);
+            l_part[0] += e0;
+            l_part[1] += e1;
+          }
           pf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
         }
       }
-
-      // O^T += V_j^T P^T
+    }
+    if constexpr (HAS_NXT && HAS_CUR) {
+      // interleave: a few K reads ahead, then {1 MFMA, ~6 VALU, 1 K read}
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
 #pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk) {
+      for (int i = 0; i < NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+      }
+    }
+    if constexpr (HAS_CUR) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
           const __bf16* vb = vt + kk * 16 * D + voff[db];
@@ -276,14 +296,59 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
                                                             oacc[db], 0, 0, 0);
         }
       }
+      // V reads two MFMAs ahead of their use
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 1);
+#pragma unroll
+      for (int i = 0; i < NKK * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+      }
     }
+  };
 
-    if (j + 1 < wg_tiles) stash(buf ^ 1);
+  // ---- pipeline ------------------------------------------------------------
+  // iteration j (-1 <= j < wg_tiles): loads K_{j+2}, V_{j+1}; the wave
+  // finishes tile j (softmax + P.V, reading V buffer j&1) and starts tile j+1
+  // (S^T, reading K buffer (j+1)&1).  Buffers written in iteration j were
+  // last read in iteration j-1, before the barrier that ends it.
+  if (wg_tiles > 0) load_k(0, 0);
+  wait_loads();
+  __syncthreads();
+
+#pragma clang loop unroll(disable)
+  for (int j = -1; j < wg_tiles; ++j) {
+    // K_{j+2} -> K buffer j&1 and V_{j+1} -> V buffer (j+1)&1: both were last
+    // read in iteration j-1
+    if (j + 2 < wg_tiles) load_k(j + 2, j & 1);
+    if (j + 1 < wg_tiles) load_v(j + 1, (j + 1) & 1);
+
+    const bool cur = j >= 0 && j < wv_tiles;
+    const bool nxt = j + 1 < wv_tiles;
+    const __bf16* kt = ks_base + ((j + 1) & 1) * BC * D;
+    const __bf16* vt = vs_base + (j & 1) * BC * D;
+    if (cur) {
+      const int kv0 = j * BC;
+      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+      if (masked)
+        stats(std::true_type{}, kv0);
+      else
+        stats(std::false_type{}, kv0);
+      if (nxt)
+        step(std::true_type{}, std::true_type{}, kt, vt);
+      else
+        step(std::true_type{}, std::false_type{}, kt, vt);
+    } else if (nxt) {
+      step(std::false_type{}, std::true_type{}, kt, vt);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
+
+    wait_loads();
     __syncthreads();
   }
 
   // ---- epilogue: O = acc / l -> bf16, lse = ln2 * (m_ref + log2 l)
-  const float l_tot = pair_sum(l_part);   // wave-uniform exchange, before any lane test
+  const float l_tot = pair_sum(l_part[0] + l_part[1]);   // wave-uniform, before any lane test
   if (myq < N) {
     const float inv = 1.f / l_tot;
     __bf16* og = (__bf16*)p.o + head_base + (long long)myq * tok;
@@ -304,13 +369,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   }
 }
 
-}  // namespace attn
-
 // ---------------------------------------------------------------------------
 // host-side launch helpers (called by the C ABI in attn_api.cpp)
 // ---------------------------------------------------------------------------
-namespace attn {
-
 template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_bf16_t(const FwdParams& prm, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BC, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream,
@@ -318,16 +379,18 @@ static hipError_t launch_bf16_t(const FwdParams& prm, int grid, hipStream_t stre
   return hipGetLastError();
 }
 
-// Rows per work-group for each head dim (queries = 32 per wave).
-int bf16_rows_per_block(int d) { return d == 128 ? 8 * 32 : 8 * 32; }
+// Waves per work-group: 8 (two per SIMD).
+constexpr int kBf16Waves = 8;
+
+int bf16_rows_per_block(int d) { return kBf16Waves * 32; }
 
 hipError_t launch_bf16(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream) {
   if (d == 128) {
-    return causal ? launch_bf16_t<128, 8, 64, true>(prm, grid, stream)
-                  : launch_bf16_t<128, 8, 64, false>(prm, grid, stream);
+    return causal ? launch_bf16_t<128, kBf16Waves, 64, true>(prm, grid, stream)
+                  : launch_bf16_t<128, kBf16Waves, 64, false>(prm, grid, stream);
   }
-  return causal ? launch_bf16_t<64, 8, 64, true>(prm, grid, stream)
-                : launch_bf16_t<64, 8, 64, false>(prm, grid, stream);
+  return causal ? launch_bf16_t<64, kBf16Waves, 64, true>(prm, grid, stream)
+                : launch_bf16_t<64, kBf16Waves, 64, false>(prm, grid, stream);
 }
 
 }  // namespace attn

@@ -9,6 +9,7 @@ namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
@@ -69,11 +70,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16x2 (round to nearest even), one v_cvt_pk_bf16_f32;
+// a in the low half
 __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a;
-  __bf16 y = (__bf16)b;
-  return (unsigned)__builtin_bit_cast(unsigned short, x) |
-         ((unsigned)__builtin_bit_cast(unsigned short, y) << 16);
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
 }  // namespace attn

@@ -17,8 +17,8 @@ import numpy as np
 import pytest
 import torch
 
-from parity_common import (assert_bf16_ok, assert_fp8_ok, errors, reference, require_gpu,
-                           run_bf16, run_fp8)
+from parity_common import (assert_bf16_ok, assert_fp8_ok, errors, fp8_lse_bound, reference,
+                           require_gpu, run_bf16, run_fp8)
 from workloads import WORKLOADS, Workload, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -39,12 +39,13 @@ def _run(w, inp, causal, scale=None, shape=None):
     return run_bf16(inp, B, H, N, d, causal, scale)
 
 
-def _check(w, out, err, label):
+def _check(w, inp, out, ro, rl, causal, scale, label, rows=None):
     assert out.guards_intact(), label + ": wrote outside O/LSE"
     if w.dtype == "fp8":
-        assert_fp8_ok(err, label)
+        bound = fp8_lse_bound(inp, causal, scale, rows)
+        assert_fp8_ok(errors(out, ro, rl, rows, lse_bound=bound), label)
     else:
-        assert_bf16_ok(err, label)
+        assert_bf16_ok(errors(out, ro, rl, rows), label)
 
 
 # ---------------------------------------------------------------------------
@@ -63,7 +64,7 @@ def test_edge_shapes(dtype, d, causal, B, H, N):
     inp = make_inputs(w)
     out = _run(w, inp, causal)
     ro, rl = reference(inp, dtype, causal, w.scale)
-    _check(w, out, errors(out, ro, rl), "edge %s d=%d causal=%d B=%d H=%d N=%d" %
+    _check(w, inp, out, ro, rl, causal, w.scale, "edge %s d=%d causal=%d B=%d H=%d N=%d" %
            (dtype, d, causal, B, H, N))
 
 
@@ -75,7 +76,7 @@ def test_scale_sign_and_zero(dtype, scale, causal):
     inp = make_inputs(w)
     out = _run(w, inp, causal, scale=scale)
     ro, rl = reference(inp, dtype, causal, scale)
-    _check(w, out, errors(out, ro, rl), "scale %s %g causal=%d" % (dtype, scale, causal))
+    _check(w, inp, out, ro, rl, causal, scale, "scale %s %g causal=%d" % (dtype, scale, causal))
 
 
 # ---------------------------------------------------------------------------
@@ -93,7 +94,7 @@ def test_workload(name, causal):
     out = _run(w, inp, causal)
     rows = None if w.N <= 2048 else sample_rows(w)
     ro, rl = reference(inp, w.dtype, causal, w.scale, rows=rows)
-    _check(w, out, errors(out, ro, rl, rows), "%s causal=%d" % (name, causal))
+    _check(w, inp, out, ro, rl, causal, w.scale, "%s causal=%d" % (name, causal), rows)
 
 
 # ---------------------------------------------------------------------------
