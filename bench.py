@@ -1,6 +1,6 @@
 """Throughput of the tiled exact attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long8k]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload long8k]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one pass of the whole hot path -- one attn_fwd (or attn_fwd_fp8)
@@ -30,32 +30,40 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz dense MFMA
 METRIC = "attn fwd TFLOPS (4BHN²d, causal halved) + % of MI355X MFMA peak, 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
-def kernel_source_hash():
+KERNEL_SOURCES = {"bf16": ("attn_fwd_bf16.hip", "attn_kernels.hpp", "attn_api.cpp"),
+                  "fp8": ("attn_fwd_fp8.hip", "attn_kernels.hpp", "attn_api.cpp")}
+
+
+def kernel_source_hash(dtype):
+    """Hash of the sources the dtype's kernel is built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_attention_tile_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[dtype]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, causal):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources; else None."""
+def measured_traffic(workload, dtype, causal):
+    """HBM bytes per launch from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain
+    copy), if they were taken on the current kernel sources; else None."""
+    key = "%s_%s" % (workload, "causal" if causal else "noncausal")
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            for line in f:
+                fields = line.split()
+                if len(fields) == 7 and fields[0] == key:
+                    if fields[1] != kernel_source_hash(dtype):
+                        return None
+                    return int(fields[6])
     except (OSError, ValueError):
         return None
-    key = "%s_%s" % (workload, "causal" if causal else "noncausal")
-    ent = rec.get(key)
-    if not ent or ent.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return ent.get("hbm_bytes_per_launch")
+    return None
 
 
 def _one_head(w, inp, causal, b, h, rows):
@@ -74,9 +82,10 @@ def _one_head(w, inp, causal, b, h, rows):
 
 def cpu_baseline(w, inp, causal, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the same workload:
-    seeded query rows of the workload's heads, as many as fit in about
-    ``budget_s`` seconds (a first pass of 512 rows per head sizes the
-    sample)."""
+    seeded query rows of every head of the workload, as many per head as fit
+    in about ``budget_s`` seconds.  A 512-row probe sizes a first pass; a pass
+    that ends in under half the budget is discarded and repeated with the
+    row count scaled up (at most twice)."""
     import numpy as np
     from workloads import sample_rows
     try:
@@ -85,26 +94,29 @@ def cpu_baseline(w, inp, causal, budget_s=12.0):
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    # size the sample: time 512 rows of the first head, then pick the row
-    # count per head that fills the budget over all heads
     probe = sample_rows(w, count=min(512, w.N))
+    _one_head(w, inp, causal, 0, 0, probe[0, 0])          # thread pools warm up
     t0 = time.perf_counter()
     _one_head(w, inp, causal, 0, 0, probe[0, 0])
     per_row = (time.perf_counter() - t0) / probe.shape[2]
     count = int(min(w.N, max(512, budget_s / max(per_row, 1e-9) / len(heads))))
-    rows = sample_rows(w, count=count)
-    flops = 0.0
-    done = 0
-    t0 = time.perf_counter()
-    for (b, h) in heads:
-        r = rows[b, h]
-        _one_head(w, inp, causal, b, h, r)
-        vis = (r + 1) if causal else np.full(r.shape, w.N)
-        flops += float(4.0 * w.d * vis.sum())
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
+    for attempt in range(3):
+        rows = sample_rows(w, count=count)
+        flops = 0.0
+        done = 0
+        t0 = time.perf_counter()
+        for (b, h) in heads:
+            r = rows[b, h]
+            _one_head(w, inp, causal, b, h, r)
+            vis = (r + 1) if causal else np.full(r.shape, w.N)
+            flops += float(4.0 * w.d * vis.sum())
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * budget_s or count >= w.N or attempt == 2:
             break
-    dt = time.perf_counter() - t0
+        count = int(min(w.N, count * budget_s / max(dt, 1e-3)))
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOPS",
@@ -119,8 +131,8 @@ def cpu_baseline(w, inp, causal, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long8k")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -228,7 +240,7 @@ def main():
                    "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(w.name, causal),
+                     "traffic": measured_traffic(w.name, w.dtype, causal),
                      "kernel_avg_ms": round(avg_launch_ms, 4)},
     }
     if not args.no_cpu_baseline:

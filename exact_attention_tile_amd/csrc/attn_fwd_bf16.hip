@@ -12,7 +12,7 @@
 //   one work-group = NW waves = 32*NW query rows of one (batch, head);
 //   one wave       = 32 query rows, for which it owns the output tile;
 //   K/V tiles of BC keys are streamed HBM -> LDS (global_load_lds, no
-//   registers), double buffered, one barrier per tile.
+//   registers), double buffered, two barriers per tile (see below).
 //
 // Transposed formulation.  Each wave computes S^T = K_j Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T kept in VGPRs for
@@ -28,11 +28,15 @@
 // with two ds_read_b64_tr_b16 (transposing LDS reads of 4 rows x 16 columns
 // per 16-lane group).
 //
-// Overlap inside a wave (software pipeline).  K runs one tile ahead of V: in
-// step j a wave issues the S^T product of tile j+1 on the matrix cores and,
-// interleaved with those MFMAs in its instruction stream, the exponentials of
-// tile j on the vector ALU; then the P.V product of tile j.  Two waves share
-// each SIMD and fill each other's gaps.
+// Overlap between the two waves of a SIMD (ping-pong).  Waves i and i+4 of
+// the work-group share a SIMD; waves 0-3 form group A and waves 4-7 group B.
+// The tile loop runs in phases separated by work-group barriers, two per
+// K/V tile, and group B runs one phase behind group A.  Each wave alternates
+//   X_j : S^T of tile j+1 = K_{j+1} Q^T and O^T += V_j^T P_j^T  (matrix cores)
+//   Y_j : row max, gated rescale and exponentials of tile j+1   (vector ALU)
+// so in every phase one wave of each SIMD is on the matrix cores while the
+// other is on the vector ALU.  Group B also issues the LDS-bound loads in its
+// Y phases, two phases before the data is needed.
 //
 // Softmax in base 2: scores are kept as s*c with c = |scale|*log2(e) folded
 // into one fma; p = exp2(s*c - m_ref) on v_exp_f32.  m_ref only moves when a
@@ -61,32 +65,26 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
   return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
-// sched_group_barrier masks
-constexpr int kSchedVALU = 0x002;
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedDSRead = 0x100;
-
 template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BC == 64, "kv tile");
-  constexpr int T = NW * 64;             // threads
+  static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
   constexpr int BR = NW * 32;            // query rows per work-group
-  constexpr int CPR = D / 8;             // 16-byte chunks per row
-  constexpr int CPT = BC * CPR / T;      // chunks per thread per tensor per tile
-  static_assert(CPT * T == BC * CPR, "tile must split evenly over threads");
   constexpr int NKB = BC / 32;           // 32-key blocks per tile
   constexpr int NDB = D / 32;            // 32-wide column blocks of the output
   constexpr int NKS = D / 16;            // k-steps of the QK^T product
   constexpr int NKK = BC / 16;           // 16-key steps of the P.V product
+  constexpr int TILE = BC * D;           // elements per K or V tile
 
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * BC * D];
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];
   __bf16* ks_base = smem;                // K tiles: [2][BC][D]
-  __bf16* vs_base = smem + 2 * BC * D;   // V tiles: [2][BC][D]
+  __bf16* vs_base = smem + 2 * TILE;     // V tiles: [2][BC][D]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int grp = wave >> 2;             // 0: group A, 1: group B
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
@@ -129,40 +127,57 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
   }
 
-  // ---- tile loader: global_load_lds_dwordx4 straight into the swizzled LDS
-  // tile.  One instruction fills 1 KiB of LDS, lane l writing bytes
-  // [16 l, 16 l + 16) after the wave-uniform base; so the swizzle is applied
-  // by choosing each lane's source chunk.  Rows past N are clamped to row
-  // N-1: their keys are masked, so they contribute p = 0 against finite V.
-  constexpr int LPW = BC * D * 2 / 1024 / NW;          // loads per wave per tensor per tile
-  static_assert(LPW * 1024 * NW == BC * D * 2, "tile must split into 1 KiB per wave");
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  int ld_row[LPW], ld_kcol[LPW], ld_vcol[LPW];
+  // ---- tile loader (group B only): global_load_lds_dwordx4 straight into
+  // the swizzled LDS tile.  One instruction fills 1 KiB of LDS, lane l
+  // writing bytes [16 l, 16 l + 16) after the wave-uniform base (M0), so the
+  // swizzle is applied by choosing each lane's source chunk.  Rows past N are
+  // clamped to row N-1: their keys are masked, so they contribute p = 0
+  // against finite V.  The loads are issued with inline asm so that the
+  // compiler does not serialise them against LDS reads of the other buffer;
+  // their completion is awaited explicitly (vmcnt) before a barrier.
+  constexpr int LPW = TILE * 2 / 1024 / 4;              // loads per B wave per tensor per tile
+  static_assert(LPW * 1024 * 4 == TILE * 2, "tile must split into 1 KiB per load");
+  const int wb = wave & 3;                               // index within the group
+  int ld_row[LPW];
+  unsigned kgo[LPW], vgo[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int off = (wave * LPW + i) * 512 + lane * 8;   // element offset in the tile
+    const int off = (wb * LPW + i) * 512 + lane * 8;     // element offset in the tile
     const int row = off / D;
     const int pc = (off - row * D) / 8;                   // physical 16-byte chunk
     ld_row[i] = row;
-    ld_kcol[i] = (pc ^ swz_k<D>(row)) * 8;
-    ld_vcol[i] = (pc ^ swz_v<D>(row)) * 8;
+    kgo[i] = (unsigned)(((long long)row * tok + (pc ^ swz_k<D>(row)) * 8) * 2);
+    vgo[i] = (unsigned)(((long long)row * tok + (pc ^ swz_v<D>(row)) * 8) * 2);
   }
-  auto load_tile = [&](const __bf16* src, const int* col, __bf16* dst_tile, int j) {
+  const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS __bf16*)ks_base);
+  const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS __bf16*)vs_base);
+  const unsigned lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wb * LPW * 1024));
+  auto load_tile = [&](const unsigned* go, const __bf16* src, unsigned lds_buf, int j) {
     const int kv0 = j * BC;
+    const unsigned la0 = lds_buf + lds_wave;
+    if (kv0 + BC <= N) {
+      const __bf16* base = src + (long long)kv0 * tok;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int n = min(kv0 + ld_row[i], N - 1);
-      const __bf16* g = src + (long long)n * tok + col[i];
-      __bf16* l = dst_tile + (wave_u * LPW + i) * 512;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                       (ATTN_LDS void*)l, 16, 0, 0);
+      for (int i = 0; i < LPW; ++i)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
+                     "v"(go[i]), "s"(base)
+                     : "memory");
+    } else {
+      // ragged last tile: clamp the rows (64-bit addresses)
+      const __bf16* base = src + (long long)kv0 * tok;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const long long back = (long long)(kv0 + ld_row[i] < N ? 0 : kv0 + ld_row[i] - (N - 1)) * tok;
+        const __bf16* g = base + (long long)(go[i] / 2) - back;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
+                     "v"(g)
+                     : "memory");
+      }
     }
   };
-  auto load_k = [&](int j, int buf) { load_tile(kg, ld_kcol, ks_base + buf * BC * D, j); };
-  auto load_v = [&](int j, int buf) { load_tile(vg, ld_vcol, vs_base + buf * BC * D, j); };
-  // vmcnt(0): this wave's LDS-bound loads have landed (before the barrier
-  // that publishes them)
-  auto wait_loads = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  auto load_k = [&](int j) { load_tile(kgo, kg, lds_k + (unsigned)((j & 1) * TILE * 2), j); };
+  auto load_v = [&](int j) { load_tile(vgo, vg, lds_v + (unsigned)((j & 1) * TILE * 2), j); };
+  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // ---- per-lane LDS read offsets (elements)
   // K A-operand: row kb*32+ln, chunk 2ks+lh (swizzled by the row)
@@ -188,98 +203,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   float m_ref = -__builtin_inff();   // reference max, log2 units
   float l_part[2] = {0.f, 0.f};      // this lane-half's share of the row sum (2 chains)
   const float c = p.c;
-  f32x16 s_cur[NKB];                 // S^T of the tile being finished
-  f32x16 s_nxt[NKB];                 // S^T of the next tile (in flight)
+  f32x16 s[NKB];                     // S^T of the tile whose softmax is next
+  bf16x8 pf[NKK];                    // P of the tile whose P.V is next
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-    s_cur[kb] = f32x16{};
-    s_nxt[kb] = f32x16{};
-  }
+  for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) pf[kk] = bf16x8{};
 
-  // ---- pieces of one pipeline step ----------------------------------------
-  // row max of s_cur (with the mask when MASKED) and the gated rescale of
-  // m_ref / l_part / oacc
-  auto stats = [&](auto masked_tag, int kv0) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
-      // off - 4*lh <= lim
-      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
+  // ---- X_j: S^T of tile j+1 (K tile kt) and O^T += V_j^T P_j^T (V tile vt)
+  auto phase_x = [&](auto qk_tag, auto pv_tag, const __bf16* kt, const __bf16* vt) {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
+    if constexpr (QK) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s_cur[kb][r] = -__builtin_inff();
-    }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s_cur[kb][r]), s_cur[kb][r + 1]);
-    mx = pair_max(mx);
-    const float mt = mx * c;
-    const bool need = mt > m_ref + kTauBf16;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
-      m_ref = need ? mt : m_ref;
-      l_part[0] *= alpha;
-      l_part[1] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    }
-  };
-
-  // S^T of the next tile (K buffer kt) into s_nxt, interleaved with the
-  // exponentials of s_cur (when HAS_CUR); then, when HAS_CUR,
-  // O^T += V^T P^T from V buffer vt.
-  auto step = [&](auto cur_tag, auto nxt_tag, const __bf16* kt, const __bf16* vt) {
-    constexpr bool HAS_CUR = decltype(cur_tag)::value;
-    constexpr bool HAS_NXT = decltype(nxt_tag)::value;
-    bf16x8 pf[NKK];
-    if constexpr (HAS_NXT) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s_nxt[kb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int kb = 0; kb < NKB; ++kb) {
           bf16x8 a = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
-          s_nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s_nxt[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : s[kb], 0,
+                                                         0, 0);
         }
       }
     }
-    if constexpr (HAS_CUR) {
-      const float neg_m = -m_ref;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 w;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int r = half * 8 + 2 * t;
-            const float e0 = fast_exp2(__builtin_fmaf(s_cur[kb][r], c, neg_m));
-            const float e1 = fast_exp2(__builtin_fmaf(s_cur[kb][r + 1], c, neg_m));
-            w[t] = pack_bf16x2(e0, e1);
-            l_part[0] += e0;
-            l_part[1] += e1;
-          }
-          pf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-    }
-    if constexpr (HAS_NXT && HAS_CUR) {
-      // interleave: a few K reads ahead, then {1 MFMA, ~6 VALU, 1 K read}
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 3, 0);
-#pragma unroll
-      for (int i = 0; i < NKB * NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-      }
-    }
-    if constexpr (HAS_CUR) {
+    if constexpr (PV) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
@@ -296,54 +242,122 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
                                                             oacc[db], 0, 0, 0);
         }
       }
-      // V reads two MFMAs ahead of their use
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 1);
+    }
+    // keep several LDS fragments in flight ahead of the MFMAs that consume
+    // them (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA)
+    if constexpr (QK && PV) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
 #pragma unroll
       for (int i = 0; i < NKK * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 1);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
   };
 
-  // ---- pipeline ------------------------------------------------------------
-  // iteration j (-1 <= j < wg_tiles): loads K_{j+2}, V_{j+1}; the wave
-  // finishes tile j (softmax + P.V, reading V buffer j&1) and starts tile j+1
-  // (S^T, reading K buffer (j+1)&1).  Buffers written in iteration j were
-  // last read in iteration j-1, before the barrier that ends it.
-  if (wg_tiles > 0) load_k(0, 0);
+  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, row max, gated rescale
+  // of m_ref / l / O, exponentials -> pf
+  auto phase_y = [&](auto masked_tag, int kv0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
+      // off - 4*lh <= lim
+      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+    mx = pair_max(mx);
+    const float mt = mx * c;
+    const bool need = mt > m_ref + kTauBf16;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
+      m_ref = need ? mt : m_ref;
+      l_part[0] *= alpha;
+      l_part[1] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = half * 8 + 2 * t;
+          const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+          const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, neg_m));
+          w[t] = pack_bf16x2(e0, e1);
+          l_part[0] += e0;
+          l_part[1] += e1;
+        }
+        pf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+  };
+
+  // ---- phase loop ------------------------------------------------------------
+  // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
+  // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
+  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u in phase 2u (into
+  // buffers last read in phases 2u-2 / 2u-1) and waits for them at the end
+  // of phase 2u+1.
+  if (grp == 1 && wg_tiles > 0) load_k(0);
   wait_loads();
   __syncthreads();
 
-#pragma clang loop unroll(disable)
-  for (int j = -1; j < wg_tiles; ++j) {
-    // K_{j+2} -> K buffer j&1 and V_{j+1} -> V buffer (j+1)&1: both were last
-    // read in iteration j-1
-    if (j + 2 < wg_tiles) load_k(j + 2, j & 1);
-    if (j + 1 < wg_tiles) load_v(j + 1, (j + 1) & 1);
-
-    const bool cur = j >= 0 && j < wv_tiles;
-    const bool nxt = j + 1 < wv_tiles;
-    const __bf16* kt = ks_base + ((j + 1) & 1) * BC * D;
-    const __bf16* vt = vs_base + (j & 1) * BC * D;
-    if (cur) {
-      const int kv0 = j * BC;
-      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-      if (masked)
-        stats(std::true_type{}, kv0);
-      else
-        stats(std::false_type{}, kv0);
-      if (nxt)
-        step(std::true_type{}, std::true_type{}, kt, vt);
-      else
-        step(std::true_type{}, std::false_type{}, kt, vt);
-    } else if (nxt) {
-      step(std::false_type{}, std::true_type{}, kt, vt);
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  const int n_phases = 2 * wg_tiles + 2;
+  for (int ph = 0; ph < n_phases; ++ph) {
+    if (grp == 1 && (ph & 1) == 0) {
+      const int u = ph >> 1;
+      if (u + 1 < wg_tiles) load_k(u + 1);
+      if (u < wg_tiles) load_v(u);
     }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s_cur[kb] = s_nxt[kb];
-
-    wait_loads();
+    const int q = ph - grp;
+    if (q >= 0) {
+      if ((q & 1) == 0) {
+        const int j = (q >> 1) - 1;
+        const bool qk = j + 1 < wv_tiles;
+        const bool pv = j >= 0 && j < wv_tiles;
+        const __bf16* kt = ks_base + ((j + 1) & 1) * TILE;
+        const __bf16* vt = vs_base + (j & 1) * TILE;
+        if (qk && pv)
+          phase_x(T_{}, T_{}, kt, vt);
+        else if (qk)
+          phase_x(T_{}, F_{}, kt, vt);
+        else if (pv)
+          phase_x(F_{}, T_{}, kt, vt);
+      } else {
+        const int j = (q - 3) / 2;
+        if (j + 1 < wv_tiles) {
+          const int kv0 = (j + 1) * BC;
+          const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+          if (masked)
+            phase_y(T_{}, kv0);
+          else
+            phase_y(F_{}, kv0);
+        }
+      }
+    }
+    if (grp == 1 && (ph & 1) == 1) wait_loads();
     __syncthreads();
   }
 
@@ -379,7 +393,7 @@ static hipError_t launch_bf16_t(const FwdParams& prm, int grid, hipStream_t stre
   return hipGetLastError();
 }
 
-// Waves per work-group: 8 (two per SIMD).
+// Waves per work-group: 8 (two per SIMD, one of each ping-pong group).
 constexpr int kBf16Waves = 8;
 
 int bf16_rows_per_block(int d) { return kBf16Waves * 32; }
