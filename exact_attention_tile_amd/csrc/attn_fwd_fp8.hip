@@ -1,25 +1,29 @@
 // OCP FP8 E4M3 tiled exact attention forward for gfx950 (MI355X, CDNA4).
 //
-// Same method and work decomposition as the bf16 kernel (attn_fwd_bf16.hip):
-// online softmax over K/V tiles with a threshold-gated rescale, transposed
-// products S^T = K Q^T and O^T += V^T P^T so each lane owns one query column.
-// The FP8 operands with fp32 accumulation follow "FlashAttention-3: Pipeline
-// Assíncrono com Warp Specialization, WGMMA e FP8 no Hopper e Blackwell",
-// section "Estabilidade em FP8: Algoritmo de 2 Passos e Incoherent
-// Processing" (E4M3: 1 sign, 4 exponent, 3 mantissa bits, range +-448).
+// Same method, work decomposition and wave schedule as the bf16 kernel
+// (attn_fwd_bf16.hip): online softmax over K/V tiles with a threshold-gated
+// rescale, transposed products S^T = K Q^T and O^T += V^T P^T so that each
+// lane owns one query column, K/V tiles streamed HBM -> LDS with
+// global_load_lds (no VGPR staging), and the two-group ping-pong over each
+// SIMD's wave pair.  The FP8 operands with fp32 accumulation follow
+// "FlashAttention-3: Pipeline Assíncrono com Warp Specialization, WGMMA e FP8
+// no Hopper e Blackwell", section "Estabilidade em FP8: Algoritmo de 2 Passos
+// e Incoherent Processing" (E4M3: 1 sign, 4 exponent, 3 mantissa bits,
+// range +-448).
 //
 // Products: v_mfma_f32_32x32x64_f8f6f4 (both operands e4m3).  Lane (m, h)
 // of an operand holds 32 consecutive k-slots 32h .. 32h+31.
 //  * S^T: A = K rows (32 bytes of one key row per lane, two ds_read_b128),
 //    B = Q^T (32 bytes of the lane's query row, in VGPRs).
-//  * P^T: lane-half h owns, in the S^T accumulators of a 64-key tile, the
+//  * P^T: lane-half h owns, in the S^T accumulators of a 64-key step, the
 //    keys 8g + 4h + e (g = 0..7, e = 0..3); slot t = 4g + e of its B operand
 //    holds key 8g + 4h + e, i.e. accumulator register t of block t/16 in
 //    natural order.
-//  * V^T: the A operand needs, per lane, 32 keys of one column.  V rows are
-//    therefore stored in LDS under the key permutation
+//  * V^T: the A operand needs, per lane, 32 keys of one column.  Within each
+//    64-key step V rows are stored in LDS under the key permutation
 //        rho(8g + 4h + e) = 32h + 4g + e,
-//    which makes a lane-half's 32 keys 32 consecutive LDS rows, and are read
+//    which makes a lane-half's 32 keys 32 consecutive LDS rows; the tile
+//    loader applies it by choosing each lane's source row.  They are read
 //    with four ds_read_b64_tr_b8 (transposing LDS reads: in each 16-lane
 //    group, 8 rows x 16 columns, one column of 8 rows per lane).
 // Scaling: x = code * descale[b,h].  Scores use c = |scale| log2(e) dq dk;
@@ -27,6 +31,8 @@
 // 2^(TAU + P_OFFSET) = 256 < 448, rounded to e4m3 (RNE, v_cvt_pk_fp8_f32);
 // the row sum l is accumulated from the fp32 p'; O = acc * dv / l, so the
 // 2^P_OFFSET factor cancels; lse = ln2 * (m_ref - P_OFFSET + log2 l).
+#include <type_traits>
+
 #include "attn_kernels.hpp"
 
 namespace attn {
@@ -34,8 +40,8 @@ namespace attn {
 constexpr float kTauFp8 = 4.0f;
 constexpr float kPOffset = 4.0f;   // kTauFp8 + kPOffset <= 8 keeps p' <= 256
 
-// 16-byte-chunk XOR swizzles of the row-major [64][D]-byte LDS tiles (rows
-// of D bytes; 16 chunks of a 256-byte bank line span 256/D rows).
+// 16-byte-chunk XOR swizzles of the row-major [BC][D]-byte LDS tiles (rows
+// of D bytes; a 256-byte bank line spans 256/D rows).
 //  K: 16 lanes read one chunk of 16 consecutive rows (ds_read_b128).
 //  V: 32 lanes read 2 adjacent chunks of 8 consecutive rows (tr_b8).
 template <int D> __device__ __forceinline__ int swz_k8(int row) {
@@ -44,9 +50,9 @@ template <int D> __device__ __forceinline__ int swz_k8(int row) {
 template <int D> __device__ __forceinline__ int swz_v8(int row) {
   return D == 128 ? (((row >> 1) & 3) << 1) : (((row >> 2) & 1) << 1);
 }
-// LDS row of tile key kappa (0..63) in the V tile.
-__device__ __forceinline__ int v_perm_row(int kappa) {
-  return 32 * ((kappa >> 2) & 1) + 4 * (kappa >> 3) + (kappa & 3);
+// tile key of LDS row r of a V tile (inverse of rho within each 64-key step)
+__device__ __forceinline__ int v_row_key(int r) {
+  return (r & ~63) + 8 * ((r >> 2) & 7) + 4 * ((r >> 5) & 1) + (r & 3);
 }
 
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
@@ -54,27 +60,26 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
-  constexpr int BC = 64;                 // keys per tile (one 64-deep P.V product)
-  constexpr int T = NW * 64;
-  constexpr int BR = NW * 32;
-  constexpr int CPR = D / 16;            // 16-byte chunks per row
-  constexpr int NCH = BC * CPR;          // chunks per tensor per tile
-  constexpr int CPT = NCH >= T ? NCH / T : 1;
-  static_assert(NCH >= T ? (CPT * T == NCH) : true, "tile must split evenly over threads");
-  constexpr int NKB = BC / 32;
-  constexpr int NDB = D / 32;
-  constexpr int NKS = D / 64;
+  static_assert(BC == 64 || BC == 128, "kv tile");
+  static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
+  constexpr int BR = NW * 32;            // query rows per work-group
+  constexpr int NKB = BC / 32;           // 32-key blocks per tile
+  constexpr int NKK = BC / 64;           // 64-key steps of the P.V product
+  constexpr int NDB = D / 32;            // 32-wide column blocks of the output
+  constexpr int NKS = D / 64;            // k-steps of the QK^T product
+  constexpr int TILE = BC * D;           // bytes per K or V tile
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * BC * D];
-  unsigned char* ks_base = smem;
-  unsigned char* vs_base = smem + 2 * BC * D;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * TILE];
+  unsigned char* ks_base = smem;         // K tiles: [2][BC][D]
+  unsigned char* vs_base = smem + 2 * TILE;   // V tiles: [2][BC][D], rows permuted
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int grp = wave >> 2;             // 0: group A, 1: group B
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
@@ -97,7 +102,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   const float dq = p.dq[bh];
   const float dk = p.dk[bh];
   const float dv = p.dv[bh];
-  const float c = p.c * dq * dk;
+  // c = |scale dq dk| log2(e); a negative product flips the sign of Q
+  float c = p.c * dq * dk;
+  unsigned qsign = p.qsign;
+  if (c < 0.f) {
+    c = -c;
+    qsign ^= 0x80808080u;
+  }
+  c = fmaxf(c, 1e-30f);
 
   // ---- Q^T fragments: lane (n=ln, h=lh) holds Q[myq][64ks + 32lh .. +31]
   i32x8 qf[NKS];
@@ -106,8 +118,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     const u32x4* src = (const u32x4*)(qg + (long long)qr * tok + 32 * lh);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 a = src[4 * ks] ^ p.qsign;
-      u32x4 bq = src[4 * ks + 1] ^ p.qsign;
+      u32x4 a = src[4 * ks] ^ qsign;
+      u32x4 bq = src[4 * ks + 1] ^ qsign;
       i32x8 t;
       t[0] = a[0]; t[1] = a[1]; t[2] = a[2]; t[3] = a[3];
       t[4] = bq[0]; t[5] = bq[1]; t[6] = bq[2]; t[7] = bq[3];
@@ -115,6 +127,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     }
   }
 
+  // ---- tile range of this work-group and of this wave
   const int n_kv_all = (N + BC - 1) / BC;
   int wg_tiles = n_kv_all;
   int wv_tiles = qw0 < N ? n_kv_all : 0;
@@ -124,41 +137,54 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
   }
 
-  // ---- cooperative loader
-  u32x4 kreg[CPT], vreg[CPT];
-  auto fetch = [&](int j) {
+  // ---- tile loader (group B only): global_load_lds_dwordx4 straight into
+  // the LDS tile; lane l of a load fills bytes [16 l, 16 l + 16) after the
+  // wave-uniform base (M0), so the K swizzle and the V row permutation are
+  // applied by choosing each lane's source chunk.  Keys past N are clamped
+  // to key N-1 (masked: p = 0 against finite V).
+  constexpr int LPW = TILE / 1024 / 4;                   // loads per B wave per tensor per tile
+  static_assert(LPW >= 1 && LPW * 1024 * 4 == TILE, "tile must split into 1 KiB per load");
+  const int wb = wave & 3;
+  int k_key[LPW], v_key[LPW];
+  unsigned kgo[LPW], vgo[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int off = (wb * LPW + i) * 1024 + lane * 16;   // byte offset in the tile
+    const int row = off / D;
+    const int pc = (off - row * D) / 16;                  // physical 16-byte chunk
+    const int vk = v_row_key(row);
+    k_key[i] = row;
+    v_key[i] = vk;
+    kgo[i] = (unsigned)((long long)row * tok + (pc ^ swz_k8<D>(row)) * 16);
+    vgo[i] = (unsigned)((long long)vk * tok + (pc ^ swz_v8<D>(row)) * 16);
+  }
+  const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS unsigned char*)ks_base);
+  const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS unsigned char*)vs_base);
+  const unsigned lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wb * LPW * 1024));
+  auto load_tile = [&](const unsigned* go, const int* key, const unsigned char* src, unsigned lds_buf, int j) {
     const int kv0 = j * BC;
+    const unsigned la0 = lds_buf + lds_wave;
+    const unsigned char* base = src + (long long)kv0 * tok;
+    if (kv0 + BC <= N) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cc = tid + i * T;
-      const int row = cc / CPR;
-      const int col = cc - row * CPR;
-      const int n = kv0 + row;
-      if (cc < NCH && n < N) {
-        const long long off = (long long)n * tok + col * 16;
-        kreg[i] = *(const u32x4*)(kg + off);
-        vreg[i] = *(const u32x4*)(vg + off);
-      } else {
-        kreg[i] = u32x4{0u, 0u, 0u, 0u};
-        vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      for (int i = 0; i < LPW; ++i)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
+                     "v"(go[i]), "s"(base)
+                     : "memory");
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const long long back = (long long)(kv0 + key[i] < N ? 0 : kv0 + key[i] - (N - 1)) * tok;
+        const unsigned char* g = base + (long long)go[i] - back;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
+                     "v"(g)
+                     : "memory");
       }
     }
   };
-  auto stash = [&](int buf) {
-    unsigned char* kd = ks_base + buf * BC * D;
-    unsigned char* vd = vs_base + buf * BC * D;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cc = tid + i * T;
-      if (cc < NCH) {
-        const int row = cc / CPR;
-        const int col = cc - row * CPR;
-        const int vrow = v_perm_row(row);
-        *(u32x4*)(kd + row * D + ((col ^ swz_k8<D>(row)) * 16)) = kreg[i];
-        *(u32x4*)(vd + vrow * D + ((col ^ swz_v8<D>(vrow)) * 16)) = vreg[i];
-      }
-    }
-  };
+  auto load_k = [&](int j) { load_tile(kgo, k_key, kg, lds_k + (unsigned)((j & 1) * TILE), j); };
+  auto load_v = [&](int j) { load_tile(vgo, v_key, vg, lds_v + (unsigned)((j & 1) * TILE), j); };
+  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   // ---- per-lane LDS read offsets (bytes)
   int koff[NKS][2];
@@ -177,116 +203,178 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     voff[db] = vrow_l * D + ((chunk ^ vsw) * 16) + 8 * (gi & 1);
   }
 
+  // ---- running state
   f32x16 oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_ref = -__builtin_inff();
-  float l_part = 0.f;
-
-  if (wg_tiles > 0) {
-    fetch(0);
-    stash(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < wg_tiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < wg_tiles) fetch(j + 1);
-
-    if (j < wv_tiles) {
-      const unsigned char* kt = ks_base + buf * BC * D;
-      const unsigned char* vt = vs_base + buf * BC * D;
-      const int kv0 = j * BC;
-
-      f32x16 s[NKB];
+  float l_part[2] = {0.f, 0.f};
+  f32x16 s[NKB];
+  i32x8 pf[NKK];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
+  for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+  for (int kk = 0; kk < NKK; ++kk) pf[kk] = i32x8{};
+
+  // ---- X_j: S^T of tile j+1 (K tile kt) and O^T += V_j^T P_j^T (V tile vt)
+  auto phase_x = [&](auto qk_tag, auto pv_tag, const unsigned char* kt, const unsigned char* vt) {
+    constexpr bool QK = decltype(qk_tag)::value;
+    constexpr bool PV = decltype(pv_tag)::value;
+    if constexpr (QK) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
           u32x4 a0 = *(const u32x4*)(kt + kb * 32 * D + koff[ks][0]);
           u32x4 a1 = *(const u32x4*)(kt + kb * 32 * D + koff[ks][1]);
           i32x8 a;
           a[0] = a0[0]; a[1] = a0[1]; a[2] = a0[2]; a[3] = a0[3];
           a[4] = a1[0]; a[5] = a1[1]; a[6] = a1[2]; a[7] = a1[3];
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], s[kb], 0, 0, 0, 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, qf[ks], ks == 0 ? f32x16{} : s[kb],
+                                                                 0, 0, 0, 0, 0, 0);
         }
-      }
-
-      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-      unsigned vis = ~0u;
-      float mx = -__builtin_inff();
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= myq);
-            if (!ok) vis &= ~(1u << (kb * 16 + r));
-            mx = fmaxf(mx, ok ? s[kb][r] : -__builtin_inff());
-          }
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      }
-      mx = pair_max(mx);
-
-      const float mt = mx * c;
-      const bool need = mt > m_ref + kTauFp8;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
-        m_ref = need ? mt : m_ref;
-        l_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      }
-
-      // p' = exp2(s c - m_ref + P_OFFSET); slot t = 16 kb + r
-      const float bias = kPOffset - m_ref;
-      i32x8 pf;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          float e[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int r = 4 * w + x;
-            float y = fast_exp2(__builtin_fmaf(s[kb][r], c, bias));
-            if (masked) y = ((vis >> (kb * 16 + r)) & 1u) ? y : 0.f;
-            e[x] = y;
-            l_part += y;
-          }
-          pf[kb * 4 + w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
-        }
-      }
-
-      // O^T += V_j^T P^T
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        i32x8 a;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (ATTN_LDS i32x2*)(vt + voff[db] + 8 * u * D));
-          a[2 * u] = t[0];
-          a[2 * u + 1] = t[1];
-        }
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf, oacc[db], 0, 0, 0, 0, 0, 0);
       }
     }
+    if constexpr (PV) {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          i32x8 a;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (ATTN_LDS i32x2*)(vt + kk * 64 * D + voff[db] + 8 * u * D));
+            a[2 * u] = t[0];
+            a[2 * u + 1] = t[1];
+          }
+          oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf[kk], oacc[db], 0, 0, 0, 0, 0, 0);
+        }
+      }
+    }
+    // keep LDS reads in flight ahead of the MFMAs that consume them
+    // (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA)
+    if constexpr (QK && PV) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int i = 0; i < NKB * NKS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < NKK * NDB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+    }
+  };
 
-    if (j + 1 < wg_tiles) stash(buf ^ 1);
+  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, row max, gated rescale
+  // of m_ref / l / O, exponentials -> pf
+  auto phase_y = [&](auto masked_tag, int kv0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
+      // off - 4*lh <= lim
+      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+    mx = pair_max(mx);
+    const float mt = mx * c;
+    const bool need = mt > m_ref + kTauFp8;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
+      m_ref = need ? mt : m_ref;
+      l_part[0] *= alpha;
+      l_part[1] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    }
+    // p' = exp2(s c - m_ref + P_OFFSET); 64-key step kk, slot t = 16 (kb & 1) + r
+    const float bias = kPOffset - m_ref;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      i32x8 w;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int kb = 2 * kk + half;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float e0 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 0], c, bias));
+          const float e1 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 1], c, bias));
+          const float e2 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 2], c, bias));
+          const float e3 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 3], c, bias));
+          l_part[0] += e0 + e2;
+          l_part[1] += e1 + e3;
+          w[4 * half + g] = pack_fp8x4(e0, e1, e2, e3);
+        }
+      }
+      pf[kk] = w;
+    }
+  };
+
+  // ---- phase loop ------------------------------------------------------------
+  // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
+  // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
+  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u in phase 2u (into
+  // buffers last read in phases 2u-2 / 2u-1) and waits for them at the end
+  // of phase 2u+1.
+  if (grp == 1 && wg_tiles > 0) load_k(0);
+  wait_loads();
+  __syncthreads();
+
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  const int n_phases = 2 * wg_tiles + 2;
+  for (int ph = 0; ph < n_phases; ++ph) {
+    if (grp == 1 && (ph & 1) == 0) {
+      const int u = ph >> 1;
+      if (u + 1 < wg_tiles) load_k(u + 1);
+      if (u < wg_tiles) load_v(u);
+    }
+    const int q = ph - grp;
+    if (q >= 0) {
+      if ((q & 1) == 0) {
+        const int j = (q >> 1) - 1;
+        const bool qk = j + 1 < wv_tiles;
+        const bool pv = j >= 0 && j < wv_tiles;
+        const unsigned char* kt = ks_base + ((j + 1) & 1) * TILE;
+        const unsigned char* vt = vs_base + (j & 1) * TILE;
+        if (qk && pv)
+          phase_x(T_{}, T_{}, kt, vt);
+        else if (qk)
+          phase_x(T_{}, F_{}, kt, vt);
+        else if (pv)
+          phase_x(F_{}, T_{}, kt, vt);
+      } else {
+        const int j = (q - 3) / 2;
+        if (j + 1 < wv_tiles) {
+          const int kv0 = (j + 1) * BC;
+          const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+          if (masked)
+            phase_y(T_{}, kv0);
+          else
+            phase_y(F_{}, kv0);
+        }
+      }
+    }
+    if (grp == 1 && (ph & 1) == 1) wait_loads();
     __syncthreads();
   }
 
-  const float l_tot = pair_sum(l_part);
+  // ---- epilogue: O = acc dv / l -> bf16, lse = ln2 (m_ref - offset + log2 l)
+  const float l_tot = pair_sum(l_part[0] + l_part[1]);
   if (myq < N) {
     const float sc = dv / l_tot;
     __bf16* og = (__bf16*)p.o + head_base + (long long)myq * tok;
@@ -308,22 +396,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_fp8_t(const FwdParams& prm, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream,
                      prm);
   return hipGetLastError();
 }
 
-int fp8_rows_per_block(int d) { return (d == 128 ? 8 : 8) * 32; }
+// Waves per work-group: 8 (two per SIMD, one of each ping-pong group);
+// keys per K/V tile: 128 (two 64-deep P.V steps), which halves the barriers
+// per key of a 64-key tile and fits the register budget of the fp8 operands.
+constexpr int kFp8Waves = 8;
+constexpr int kFp8Tile = 128;
+
+int fp8_rows_per_block(int d) { return kFp8Waves * 32; }
 
 hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream) {
   if (d == 128) {
-    return causal ? launch_fp8_t<128, 8, true>(prm, grid, stream)
-                  : launch_fp8_t<128, 8, false>(prm, grid, stream);
+    return causal ? launch_fp8_t<128, kFp8Waves, kFp8Tile, true>(prm, grid, stream)
+                  : launch_fp8_t<128, kFp8Waves, kFp8Tile, false>(prm, grid, stream);
   }
-  return causal ? launch_fp8_t<64, 8, true>(prm, grid, stream)
-                : launch_fp8_t<64, 8, false>(prm, grid, stream);
+  return causal ? launch_fp8_t<64, kFp8Waves, kFp8Tile, true>(prm, grid, stream)
+                : launch_fp8_t<64, kFp8Waves, kFp8Tile, false>(prm, grid, stream);
 }
 
 }  // namespace attn
