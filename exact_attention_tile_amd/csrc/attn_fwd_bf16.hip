@@ -35,7 +35,9 @@
 //   X_j : S^T of tile j+1 = K_{j+1} Q^T and O^T += V_j^T P_j^T  (matrix cores)
 //   Y_j : row max, gated rescale and exponentials of tile j+1   (vector ALU)
 // so in every phase one wave of each SIMD is on the matrix cores while the
-// other is on the vector ALU.  Group B also issues the LDS-bound loads in its
+// other is on the vector ALU; the matrix-core wave raises its issue priority
+// (s_setprio) for the phase, so the MFMAs are never queued behind the
+// partner's vector work.  Group B also issues the LDS-bound loads in its
 // Y phases, two phases before the data is needed.
 //
 // Softmax in base 2: scores are kept as s*c with c = |scale|*log2(e) folded
@@ -214,6 +216,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   auto phase_x = [&](auto qk_tag, auto pv_tag, const __bf16* kt, const __bf16* vt) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
+    // the matrix-core phase issues first on its SIMD; the partner wave's
+    // vector ALU work fills the remaining issue slots
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (QK) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -258,6 +263,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, row max, gated rescale

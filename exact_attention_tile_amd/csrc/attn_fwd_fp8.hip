@@ -56,7 +56,9 @@ __device__ __forceinline__ int v_row_key(int r) {
 }
 
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // the untouched half of the first conversion's destination is written by
+  // the second, so its old value may be anything: reuse a's register
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -137,7 +139,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
   }
 
-  // ---- tile loader (group B only): global_load_lds_dwordx4 straight into
+  // ---- tile loader (group A only, in its matrix-core phase, whose issue
+  // slots are mostly free): global_load_lds_dwordx4 straight into
   // the LDS tile; lane l of a load fills bytes [16 l, 16 l + 16) after the
   // wave-uniform base (M0), so the K swizzle and the V row permutation are
   // applied by choosing each lane's source chunk.  Keys past N are clamped
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_ref = -__builtin_inff();
-  float l_part[2] = {0.f, 0.f};
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
   f32x16 s[NKB];
   i32x8 pf[NKK];
 #pragma unroll
@@ -220,6 +223,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   auto phase_x = [&](auto qk_tag, auto pv_tag, const unsigned char* kt, const unsigned char* vt) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
+    // the matrix-core phase issues first on its SIMD; the partner wave's
+    // vector ALU work fills the remaining issue slots
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (QK) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -267,6 +273,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, row max, gated rescale
@@ -294,15 +301,26 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
       m_ref = need ? mt : m_ref;
-      l_part[0] *= alpha;
-      l_part[1] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_part[i] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    // p' = exp2(s c - m_ref + P_OFFSET); 64-key step kk, slot t = 16 (kb & 1) + r
+    // p' = exp2(s c - m_ref + P_OFFSET), in place: all FMAs, all
+    // exponentials, then the e4m3 packs (64-key step kk, slot t = 16 (kb & 1)
+    // + r) and the row sums (four chains), so that no instruction waits on
+    // the one just before it
     const float bias = kPOffset - m_ref;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_fmaf(s[kb][r], c, bias);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(s[kb][r]);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       i32x8 w;
@@ -310,27 +328,32 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
       for (int half = 0; half < 2; ++half) {
         const int kb = 2 * kk + half;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float e0 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 0], c, bias));
-          const float e1 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 1], c, bias));
-          const float e2 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 2], c, bias));
-          const float e3 = fast_exp2(__builtin_fmaf(s[kb][4 * g + 3], c, bias));
-          l_part[0] += e0 + e2;
-          l_part[1] += e1 + e3;
-          w[4 * half + g] = pack_fp8x4(e0, e1, e2, e3);
-        }
+        for (int g = 0; g < 4; ++g)
+          w[4 * half + g] = pack_fp8x4(s[kb][4 * g], s[kb][4 * g + 1], s[kb][4 * g + 2], s[kb][4 * g + 3]);
       }
       pf[kk] = w;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l_part[r & 3] += s[kb][r];
+    // interleave: FMAs run 8 ahead of the exponentials that read them
+    // (sched_group_barrier masks: 0x002 VALU, 0x400 transcendental)
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 16 * NKB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
     }
   };
 
   // ---- phase loop ------------------------------------------------------------
   // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
   // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
-  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u in phase 2u (into
-  // buffers last read in phases 2u-2 / 2u-1) and waits for them at the end
-  // of phase 2u+1.
-  if (grp == 1 && wg_tiles > 0) load_k(0);
+  // 2t+3 (from buffer t&1).  Group A loads K_{u+1} and V_u at the start of
+  // its matrix-core phase 2u (into buffers last read in phases 2u-2 / 2u-1)
+  // and waits for them at the end of phase 2u+1.
+  if (grp == 0 && wg_tiles > 0) load_k(0);
   wait_loads();
   __syncthreads();
 
@@ -338,7 +361,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   using F_ = std::false_type;
   const int n_phases = 2 * wg_tiles + 2;
   for (int ph = 0; ph < n_phases; ++ph) {
-    if (grp == 1 && (ph & 1) == 0) {
+    if (grp == 0 && (ph & 1) == 0) {
       const int u = ph >> 1;
       if (u + 1 < wg_tiles) load_k(u + 1);
       if (u < wg_tiles) load_v(u);
@@ -369,12 +392,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
         }
       }
     }
-    if (grp == 1 && (ph & 1) == 1) wait_loads();
+    if (grp == 0 && (ph & 1) == 1) wait_loads();
     __syncthreads();
   }
 
   // ---- epilogue: O = acc dv / l -> bf16, lse = ln2 (m_ref - offset + log2 l)
-  const float l_tot = pair_sum(l_part[0] + l_part[1]);
+  const float l_tot = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   if (myq < N) {
     const float sc = dv / l_tot;
     __bf16* og = (__bf16*)p.o + head_base + (long long)myq * tok;
