@@ -70,7 +70,7 @@ template <int D> __device__ __forceinline__ int swz_v(int row) {
 template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
-  static_assert(BC == 64, "kv tile");
+  static_assert(BC == 64 || BC == 128, "kv tile");
   static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
   constexpr int BR = NW * 32;            // query rows per work-group
   constexpr int NKB = BC / 32;           // 32-key blocks per tile
@@ -400,6 +400,9 @@ static hipError_t launch_bf16_t(const FwdParams& prm, int grid, hipStream_t stre
 }
 
 // Waves per work-group: 8 (two per SIMD, one of each ping-pong group).
+// Keys per K/V tile: 64 at d = 128 (the S/P registers of a 128-key tile do
+// not fit next to the d = 128 accumulators); 128 at d = 64, which halves the
+// barriers per key.
 constexpr int kBf16Waves = 8;
 
 int bf16_rows_per_block(int d) { return kBf16Waves * 32; }
@@ -409,8 +412,8 @@ hipError_t launch_bf16(const FwdParams& prm, int d, int causal, int grid, hipStr
     return causal ? launch_bf16_t<128, kBf16Waves, 64, true>(prm, grid, stream)
                   : launch_bf16_t<128, kBf16Waves, 64, false>(prm, grid, stream);
   }
-  return causal ? launch_bf16_t<64, kBf16Waves, 64, true>(prm, grid, stream)
-                : launch_bf16_t<64, kBf16Waves, 64, false>(prm, grid, stream);
+  return causal ? launch_bf16_t<64, kBf16Waves, 128, true>(prm, grid, stream)
+                : launch_bf16_t<64, kBf16Waves, 128, false>(prm, grid, stream);
 }
 
 }  // namespace attn
