@@ -25,6 +25,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -66,65 +68,87 @@ def measured_traffic(workload, dtype, causal):
     return None
 
 
-def _one_head(w, inp, causal, b, h, rows):
-    from oracle import attention_head_rows, bf16_bits_to_float64, dequantize_e4m3
-    if w.dtype == "fp8":
-        def deq(name):
-            return dequantize_e4m3(inp[name][b:b + 1, :, h:h + 1, :],
-                                   inp["d" + name][b:b + 1, h:h + 1])[0, :, 0, :]
-        q, k, v = deq("q"), deq("k"), deq("v")
+def _head_problem(w, inp, b, h):
+    """float64 q, k, v [n][d] of (batch or sequence b, query head h), exactly
+    as the GPU sees them (the K/V head is h // (H / Hkv))."""
+    from oracle import bf16_bits_to_float64, dequantize_e4m3
+    hk = h // (w.H // w.kv_heads)
+    if w.varlen:
+        s0, s1 = int(inp["cu"][b]), int(inp["cu"][b + 1])
+        sl, bi = (slice(0, 1), slice(s0, s1)), 0
     else:
-        q = bf16_bits_to_float64(inp["q"][b, :, h, :])
-        k = bf16_bits_to_float64(inp["k"][b, :, h, :])
-        v = bf16_bits_to_float64(inp["v"][b, :, h, :])
+        sl, bi = (slice(b, b + 1), slice(None)), b
+    if w.dtype == "fp8":
+        def deq(name, head):
+            return dequantize_e4m3(inp[name][sl[0], sl[1], head:head + 1, :],
+                                   inp["d" + name][b:b + 1, head:head + 1])[0, :, 0, :]
+        return deq("q", h), deq("k", hk), deq("v", hk)
+    return (bf16_bits_to_float64(inp["q"][bi, sl[1], h, :]),
+            bf16_bits_to_float64(inp["k"][bi, sl[1], hk, :]),
+            bf16_bits_to_float64(inp["v"][bi, sl[1], hk, :]))
+
+
+def _one_head(w, inp, causal, b, h, rows):
+    from oracle import attention_head_rows
+    q, k, v = _head_problem(w, inp, b, h)
     return attention_head_rows(q, k, v, w.scale, causal, rows)
+
+
+def _rows_for(w, count, b, h, n):
+    """``count`` seeded query rows of a length-n problem (all when n <= count)."""
+    if n <= count:
+        return np.arange(n)
+    g = np.random.default_rng(1000 * w.wid + 7 + 131 * b + h)
+    return np.concatenate([[0, n - 1], np.sort(g.choice(np.arange(1, n - 1), count - 2,
+                                                        replace=False))])
 
 
 def cpu_baseline(w, inp, causal, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the same workload:
-    seeded query rows of every head of the workload, as many per head as fit
-    in about ``budget_s`` seconds.  A 512-row probe sizes a first pass; a pass
-    that ends in under half the budget is discarded and repeated with the
-    row count scaled up (at most twice)."""
-    import numpy as np
-    from workloads import sample_rows
+    seeded query rows of every (batch or sequence, head) problem, as many per
+    problem as fit in about ``budget_s`` seconds.  A 512-row probe sizes a
+    first pass; a pass that ends in under half the budget is discarded and
+    repeated with the row count scaled up (at most twice)."""
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    probe = sample_rows(w, count=min(512, w.N))
-    _one_head(w, inp, causal, 0, 0, probe[0, 0])          # thread pools warm up
+    lens = list(w.lengths) if w.varlen else [w.N] * w.B
+    heads = [(b, h) for b in range(len(lens)) for h in range(w.H) if lens[b] > 0]
+    b0 = max(range(len(lens)), key=lambda b: lens[b])
+    probe = _rows_for(w, min(512, lens[b0]), b0, 0, lens[b0])
+    _one_head(w, inp, causal, b0, 0, probe)                 # thread pools warm up
     t0 = time.perf_counter()
-    _one_head(w, inp, causal, 0, 0, probe[0, 0])
-    per_row = (time.perf_counter() - t0) / probe.shape[2]
-    count = int(min(w.N, max(512, budget_s / max(per_row, 1e-9) / len(heads))))
+    _one_head(w, inp, causal, b0, 0, probe)
+    per_row = (time.perf_counter() - t0) / probe.shape[0]
+    count = int(min(max(lens), max(512, budget_s / max(per_row, 1e-9) / len(heads))))
     for attempt in range(3):
-        rows = sample_rows(w, count=count)
         flops = 0.0
         done = 0
+        nrows = 0
         t0 = time.perf_counter()
         for (b, h) in heads:
-            r = rows[b, h]
+            r = _rows_for(w, count, b, h, lens[b])
             _one_head(w, inp, causal, b, h, r)
-            vis = (r + 1) if causal else np.full(r.shape, w.N)
+            vis = (r + 1) if causal else np.full(r.shape, lens[b])
             flops += float(4.0 * w.d * vis.sum())
             done += 1
+            nrows += r.shape[0]
             if time.perf_counter() - t0 > budget_s:
                 break
         dt = time.perf_counter() - t0
-        if dt >= 0.5 * budget_s or count >= w.N or attempt == 2:
+        if dt >= 0.5 * budget_s or count >= max(lens) or attempt == 2:
             break
-        count = int(min(w.N, count * budget_s / max(dt, 1e-3)))
+        count = int(min(max(lens), count * budget_s / max(dt, 1e-3)))
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOPS",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": "fp64 NumPy oracle on %d seeded query rows of each of %d/%d heads "
-                  "(%.2f GFLOP counted with the metric's 4*d*visible_keys per row, %.1f s)"
-                  % (rows.shape[2], done, len(heads), flops / 1e9, dt),
+        "sample": "fp64 NumPy oracle on up to %d seeded query rows of each of %d/%d (batch, head) "
+                  "problems (%d rows, %.2f GFLOP counted with the metric's 4*d*visible_keys per "
+                  "row, %.1f s)" % (count, done, len(heads), nrows, flops / 1e9, dt),
     }
 
 
@@ -146,7 +170,6 @@ def main():
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import exact_attention_tile_amd as eat
     from workloads import WORKLOADS, make_inputs
@@ -162,6 +185,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
+    Hkv, T = w.kv_heads, w.total
+    if w.varlen:
+        cu = torch.from_numpy(inp["cu"]).to(dev)
     if w.dtype == "fp8":
         q = torch.from_numpy(inp["q"]).to(dev)
         k = torch.from_numpy(inp["k"]).to(dev)
@@ -170,19 +196,33 @@ def main():
         dk = torch.from_numpy(inp["dk"]).reshape(-1).to(dev)
         dv = torch.from_numpy(inp["dv"]).reshape(-1).to(dev)
 
-        def step():
-            eat.attn_fwd_fp8(q, k, v, o, lse, dq, dk, dv, w.B, w.H, w.N, w.d, int(causal),
-                             w.scale, stream)
+        if w.varlen:
+            def step():
+                eat.attn_fwd_fp8_varlen(q, k, v, o, lse, dq, dk, dv, cu, w.B, T, w.N, w.H, Hkv,
+                                        w.d, int(causal), w.scale, stream)
+        else:
+            def step():
+                eat.attn_fwd_fp8_gqa(q, k, v, o, lse, dq, dk, dv, w.B, w.H, Hkv, w.N, w.d,
+                                     int(causal), w.scale, stream)
     else:
         def dev16(x):
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         q, k, v = dev16(inp["q"]), dev16(inp["k"]), dev16(inp["v"])
 
-        def step():
-            eat.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(causal), w.scale, stream)
+        if w.varlen:
+            def step():
+                eat.attn_fwd_varlen(q, k, v, o, lse, cu, w.B, T, w.N, w.H, Hkv, w.d, int(causal),
+                                    w.scale, stream)
+        elif Hkv != w.H:
+            def step():
+                eat.attn_fwd_gqa(q, k, v, o, lse, w.B, w.H, Hkv, w.N, w.d, int(causal), w.scale,
+                                 stream)
+        else:
+            def step():
+                eat.attn_fwd(q, k, v, o, lse, w.B, w.H, w.N, w.d, int(causal), w.scale, stream)
 
-    o = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    o = torch.empty((T, w.H, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.H, T) if w.varlen else (w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
     for _ in range(args.warmup):
         step()
@@ -235,9 +275,11 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded, workloads/)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": causal, "scale": w.scale,
-                   "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+        "config": dict({"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                        "causal": causal, "scale": w.scale,
+                        "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)"},
+                       **({"H_kv": Hkv} if Hkv != w.H else {}),
+                       **({"seq_lens": list(w.lengths), "total_tokens": T} if w.varlen else {})),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, w.dtype, causal),

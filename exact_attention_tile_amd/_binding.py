@@ -49,6 +49,15 @@ def load_library():
     lib.attn_fwd.restype = i
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_fwd_fp8.restype = i
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_gqa.restype = i
+    lib.attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_varlen.restype = i
+    lib.attn_fwd_fp8_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_fp8_gqa.restype = i
+    lib.attn_fwd_fp8_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                        f, vp]
+    lib.attn_fwd_fp8_varlen.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -100,4 +109,52 @@ def attn_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, N, d, c
                                      _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8")
+    return st
+
+
+def attn_fwd_gqa(q, k, v, o, lse, B, H, H_kv, N, d, causal, scale, stream=None, check=True):
+    """bf16 grouped-query forward; see attn_fwd_gqa in include/attn.h."""
+    st = load_library().attn_fwd_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B),
+                                     int(H), int(H_kv), int(N), int(d), int(causal), float(scale),
+                                     _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_gqa")
+    return st
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens, B, total, max_seqlen, H, H_kv, d, causal, scale,
+                    stream=None, check=True):
+    """bf16 variable-length forward; see attn_fwd_varlen in include/attn.h
+    (``cu_seqlens`` is a device int32 array of B+1 offsets)."""
+    st = load_library().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        _ptr(cu_seqlens), int(B), int(total), int(max_seqlen),
+                                        int(H), int(H_kv), int(d), int(causal), float(scale),
+                                        _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_varlen")
+    return st
+
+
+def attn_fwd_fp8_gqa(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, H_kv, N, d, causal,
+                     scale, stream=None, check=True):
+    """OCP e4m3 grouped-query forward; see attn_fwd_fp8_gqa in include/attn.h."""
+    st = load_library().attn_fwd_fp8_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                         _ptr(descale_q), _ptr(descale_k), _ptr(descale_v),
+                                         int(B), int(H), int(H_kv), int(N), int(d), int(causal),
+                                         float(scale), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8_gqa")
+    return st
+
+
+def attn_fwd_fp8_varlen(q, k, v, o, lse, descale_q, descale_k, descale_v, cu_seqlens, B, total,
+                        max_seqlen, H, H_kv, d, causal, scale, stream=None, check=True):
+    """OCP e4m3 variable-length forward; see attn_fwd_fp8_varlen in include/attn.h."""
+    st = load_library().attn_fwd_fp8_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                            _ptr(descale_q), _ptr(descale_k), _ptr(descale_v),
+                                            _ptr(cu_seqlens), int(B), int(total), int(max_seqlen),
+                                            int(H), int(H_kv), int(d), int(causal), float(scale),
+                                            _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8_varlen")
     return st

@@ -22,32 +22,50 @@ namespace {
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
-// Shared validation.  Returns ATTN_OK or the first error found.
-int validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
-             int H, int N, int d, int causal, float scale) {
+// Checks common to every entry point: the tensor pointers, the scalar
+// arguments and the sizes.  `tokens` is the number of token rows in each
+// tensor (B*N, or the packed total), H/Hkv the query and K/V heads.
+int validate(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             int64_t tokens, int H, int Hkv, int d, int causal, float scale) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_INVALID_ARG;
-  if (B <= 0 || H <= 0 || N <= 0) return ATTN_ERR_INVALID_ARG;
+  if (tokens <= 0 || H <= 0 || Hkv <= 0) return ATTN_ERR_INVALID_ARG;
+  if (H % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  // element count B*N*H*d must fit in int64 (and the per-head row offsets
-  // the kernels form from it)
+  // element count tokens*H*d must fit in int64 (and the per-head row
+  // offsets the kernels form from it)
   const int64_t lim = INT64_MAX / 4;
-  int64_t n = B;
-  if (n > lim / N) return ATTN_ERR_INVALID_ARG;
-  n *= N;
+  int64_t n = tokens;
   if (n > lim / H) return ATTN_ERR_INVALID_ARG;
   n *= H;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (n > lim / d) return ATTN_ERR_INVALID_ARG;
+  // the kernels form the byte offset of a K/V row within one tile (up to 128
+  // rows of H*d elements) in 32 bits
+  if ((int64_t)H * d > (1 << 24)) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_UNSUPPORTED;
   if (((uintptr_t)lse & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
+int validate_fixed(int B, int N, int64_t* tokens) {
+  if (B <= 0 || N <= 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B > (INT64_MAX / 4) / N) return ATTN_ERR_INVALID_ARG;
+  *tokens = (int64_t)B * N;
+  return ATTN_OK;
+}
+
+int validate_descales(const float* dq, const float* dk, const float* dv) {
+  if (!dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)dq & 3u) || ((uintptr_t)dk & 3u) || ((uintptr_t)dv & 3u)) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 // Work-group count and block order for one call.  The grid has one
-// work-group per (batch, head, query tile); it must fit the 32-bit grid.
+// work-group per (batch, head, query tile of the longest sequence); it must
+// fit the 32-bit grid.
 int plan(attn::FwdParams& prm, int rows_per_block, int* grid_out) {
-  const int64_t tiles = ((int64_t)prm.N + rows_per_block - 1) / rows_per_block;
+  const int64_t tiles = ((int64_t)prm.maxlen + rows_per_block - 1) / rows_per_block;
   const int64_t grid = (int64_t)prm.B * prm.H * tiles;
   if (grid > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
   prm.n_qtiles = (int)tiles;
@@ -63,13 +81,8 @@ void set_scale(attn::FwdParams& prm, float scale, unsigned neg_mask) {
   prm.qsign = scale < 0.f ? neg_mask : 0u;
 }
 
-}  // namespace
-
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                        int H, int N, int d, int causal, float scale, hipStream_t stream) {
-  int st = validate(q, k, v, o, lse, B, H, N, d, causal, scale);
-  if (st != ATTN_OK) return st;
-  attn::FwdParams prm = {};
+void set_common(attn::FwdParams& prm, const void* q, const void* k, const void* v, void* o,
+                float* lse, int B, int H, int Hkv) {
   prm.q = q;
   prm.k = k;
   prm.v = v;
@@ -77,42 +90,132 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   prm.lse = lse;
   prm.B = B;
   prm.H = H;
-  prm.N = N;
+  prm.Hkv = Hkv;
+  prm.group = H / Hkv;
+}
+
+int run_bf16(attn::FwdParams& prm, int d, int causal, float scale, hipStream_t stream) {
   set_scale(prm, scale, 0x80008000u);
   int grid = 0;
-  st = plan(prm, attn::bf16_rows_per_block(d), &grid);
+  const int st = plan(prm, attn::bf16_rows_per_block(d), &grid);
   if (st != ATTN_OK) return st;
-  hipError_t e = attn::launch_bf16(prm, d, causal, grid, stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return attn::launch_bf16(prm, d, causal, grid, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+int run_fp8(attn::FwdParams& prm, int d, int causal, float scale, hipStream_t stream) {
+  set_scale(prm, scale, 0x80808080u);
+  int grid = 0;
+  const int st = plan(prm, attn::fp8_rows_per_block(d), &grid);
+  if (st != ATTN_OK) return st;
+  return attn::launch_fp8(prm, d, causal, grid, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+// Fixed-length call with Hkv K/V heads.
+int fixed_params(attn::FwdParams& prm, const void* q, const void* k, const void* v, void* o,
+                 float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale) {
+  int64_t tokens = 0;
+  int st = validate_fixed(B, N, &tokens);
+  if (st != ATTN_OK) return st;
+  st = validate(q, k, v, o, lse, tokens, H, Hkv, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  set_common(prm, q, k, v, o, lse, B, H, Hkv);
+  prm.N = N;
+  prm.maxlen = N;
+  return ATTN_OK;
+}
+
+// Variable-length call.  Returns ATTN_OK with *empty = true when there is
+// nothing to compute (total == 0).
+int varlen_params(attn::FwdParams& prm, const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens, int B, int total, int max_seqlen, int H,
+                  int Hkv, int d, int causal, float scale, bool* empty) {
+  *empty = false;
+  if (B <= 0 || total < 0 || max_seqlen <= 0 || !cu_seqlens) return ATTN_ERR_INVALID_ARG;
+  if (((uintptr_t)cu_seqlens & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
+  if (total == 0) {
+    // still check the scalar arguments
+    if (H <= 0 || Hkv <= 0 || H % Hkv != 0 || (causal != 0 && causal != 1) || !isfinite(scale))
+      return ATTN_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+    *empty = true;
+    return ATTN_OK;
+  }
+  if (max_seqlen > total) return ATTN_ERR_INVALID_ARG;
+  const int st = validate(q, k, v, o, lse, total, H, Hkv, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  set_common(prm, q, k, v, o, lse, B, H, Hkv);
+  prm.cu = cu_seqlens;
+  prm.total = total;
+  prm.maxlen = max_seqlen;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int N, int d, int causal, float scale, hipStream_t stream) {
+  return attn_fwd_gqa(q, k, v, o, lse, B, H, H, N, d, causal, scale, stream);
+}
+
+extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N, int d, int causal, float scale,
+                            hipStream_t stream) {
+  attn::FwdParams prm = {};
+  const int st = fixed_params(prm, q, k, v, o, lse, B, H, H_kv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  return run_bf16(prm, d, causal, scale, stream);
+}
+
+extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int* cu_seqlens, int B, int total, int max_seqlen, int H,
+                               int H_kv, int d, int causal, float scale, hipStream_t stream) {
+  attn::FwdParams prm = {};
+  bool empty = false;
+  const int st = varlen_params(prm, q, k, v, o, lse, cu_seqlens, B, total, max_seqlen, H, H_kv, d,
+                               causal, scale, &empty);
+  if (st != ATTN_OK || empty) return st;
+  return run_bf16(prm, d, causal, scale, stream);
 }
 
 extern "C" int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                             const float* descale_q, const float* descale_k,
                             const float* descale_v, int B, int H, int N, int d, int causal,
                             float scale, hipStream_t stream) {
-  int st = validate(q, k, v, o, lse, B, H, N, d, causal, scale);
-  if (st != ATTN_OK) return st;
-  if (!descale_q || !descale_k || !descale_v) return ATTN_ERR_INVALID_ARG;
-  if (((uintptr_t)descale_q & 3u) || ((uintptr_t)descale_k & 3u) || ((uintptr_t)descale_v & 3u))
-    return ATTN_ERR_UNSUPPORTED;
+  return attn_fwd_fp8_gqa(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, H, N, d, causal,
+                          scale, stream);
+}
+
+extern "C" int attn_fwd_fp8_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const float* descale_q, const float* descale_k,
+                                const float* descale_v, int B, int H, int H_kv, int N, int d,
+                                int causal, float scale, hipStream_t stream) {
   attn::FwdParams prm = {};
-  prm.q = q;
-  prm.k = k;
-  prm.v = v;
-  prm.o = o;
-  prm.lse = lse;
+  int st = fixed_params(prm, q, k, v, o, lse, B, H, H_kv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  st = validate_descales(descale_q, descale_k, descale_v);
+  if (st != ATTN_OK) return st;
   prm.dq = descale_q;
   prm.dk = descale_k;
   prm.dv = descale_v;
-  prm.B = B;
-  prm.H = H;
-  prm.N = N;
-  set_scale(prm, scale, 0x80808080u);
-  int grid = 0;
-  st = plan(prm, attn::fp8_rows_per_block(d), &grid);
+  return run_fp8(prm, d, causal, scale, stream);
+}
+
+extern "C" int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o,
+                                   float* lse, const float* descale_q, const float* descale_k,
+                                   const float* descale_v, const int* cu_seqlens, int B,
+                                   int total, int max_seqlen, int H, int H_kv, int d, int causal,
+                                   float scale, hipStream_t stream) {
+  attn::FwdParams prm = {};
+  bool empty = false;
+  int st = varlen_params(prm, q, k, v, o, lse, cu_seqlens, B, total, max_seqlen, H, H_kv, d,
+                         causal, scale, &empty);
   if (st != ATTN_OK) return st;
-  hipError_t e = attn::launch_fp8(prm, d, causal, grid, stream);
-  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  st = validate_descales(descale_q, descale_k, descale_v);
+  if (st != ATTN_OK || empty) return st;
+  prm.dq = descale_q;
+  prm.dk = descale_k;
+  prm.dv = descale_v;
+  return run_fp8(prm, d, causal, scale, stream);
 }
 
 extern "C" const char* attn_status_string(int status) {

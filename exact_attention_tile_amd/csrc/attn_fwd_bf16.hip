@@ -94,17 +94,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   block_to_work(p, bh, qt);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
-  const int N = p.N;
-  const long long tok = (long long)p.H * D;                       // elements between tokens
-  const long long head_base = ((long long)b * N * p.H + h) * D;   // element (b, 0, h, 0)
+  SeqView sv;
+  if (!seq_view(p, D, b, h, qt * BR, sv)) return;   // whole work-group, before any barrier
+  const int N = sv.N;
+  const long long tok = (long long)p.H * D;       // elements between tokens of Q and O
+  const long long tkv = (long long)p.Hkv * D;     // elements between tokens of K and V
 
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + ln;
 
-  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + sv.q_base;
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + sv.kv_base;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + sv.kv_base;
 
   // ---- Q^T fragments (B operand): lane (n=ln, h=lh) holds Q[myq][16ks+8lh .. +7]
   bf16x8 qf[NKS];
@@ -148,8 +150,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     const int row = off / D;
     const int pc = (off - row * D) / 8;                   // physical 16-byte chunk
     ld_row[i] = row;
-    kgo[i] = (unsigned)(((long long)row * tok + (pc ^ swz_k<D>(row)) * 8) * 2);
-    vgo[i] = (unsigned)(((long long)row * tok + (pc ^ swz_v<D>(row)) * 8) * 2);
+    kgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_k<D>(row)) * 8) * 2);
+    vgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_v<D>(row)) * 8) * 2);
   }
   const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS __bf16*)ks_base);
   const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS __bf16*)vs_base);
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     const int kv0 = j * BC;
     const unsigned la0 = lds_buf + lds_wave;
     if (kv0 + BC <= N) {
-      const __bf16* base = src + (long long)kv0 * tok;
+      const __bf16* base = src + (long long)kv0 * tkv;
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
@@ -166,10 +168,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
                      : "memory");
     } else {
       // ragged last tile: clamp the rows (64-bit addresses)
-      const __bf16* base = src + (long long)kv0 * tok;
+      const __bf16* base = src + (long long)kv0 * tkv;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        const long long back = (long long)(kv0 + ld_row[i] < N ? 0 : kv0 + ld_row[i] - (N - 1)) * tok;
+        const long long back = (long long)(kv0 + ld_row[i] < N ? 0 : kv0 + ld_row[i] - (N - 1)) * tkv;
         const __bf16* g = base + (long long)(go[i] / 2) - back;
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
                      "v"(g)
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   const float l_tot = pair_sum(l_part[0] + l_part[1]);   // wave-uniform, before any lane test
   if (myq < N) {
     const float inv = 1.f / l_tot;
-    __bf16* og = (__bf16*)p.o + head_base + (long long)myq * tok;
+    __bf16* og = (__bf16*)p.o + sv.q_base + (long long)myq * tok;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       }
     }
     if (lh == 0) {
-      p.lse[(long long)bh * N + myq] = (m_ref + fast_log2(l_tot)) * 0.69314718055994531f;
+      p.lse[sv.lse_base + myq] = (m_ref + fast_log2(l_tot)) * 0.69314718055994531f;
     }
   }
 }

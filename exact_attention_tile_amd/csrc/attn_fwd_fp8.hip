@@ -89,21 +89,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   block_to_work(p, bh, qt);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
-  const int N = p.N;
-  const long long tok = (long long)p.H * D;
-  const long long head_base = ((long long)b * N * p.H + h) * D;
+  SeqView sv;
+  if (!seq_view(p, D, b, h, qt * BR, sv)) return;   // whole work-group, before any barrier
+  const int N = sv.N;
+  const long long tok = (long long)p.H * D;       // elements between tokens of Q and O
+  const long long tkv = (long long)p.Hkv * D;     // elements between tokens of K and V
 
   const int q0 = qt * BR;
   const int qw0 = q0 + wave * 32;
   const int myq = qw0 + ln;
 
-  const unsigned char* __restrict__ qg = (const unsigned char*)p.q + head_base;
-  const unsigned char* __restrict__ kg = (const unsigned char*)p.k + head_base;
-  const unsigned char* __restrict__ vg = (const unsigned char*)p.v + head_base;
+  const unsigned char* __restrict__ qg = (const unsigned char*)p.q + sv.q_base;
+  const unsigned char* __restrict__ kg = (const unsigned char*)p.k + sv.kv_base;
+  const unsigned char* __restrict__ vg = (const unsigned char*)p.v + sv.kv_base;
 
   const float dq = p.dq[bh];
-  const float dk = p.dk[bh];
-  const float dv = p.dv[bh];
+  const float dk = p.dk[b * p.Hkv + sv.hk];
+  const float dv = p.dv[b * p.Hkv + sv.hk];
   // c = |scale dq dk| log2(e); a negative product flips the sign of Q
   float c = p.c * dq * dk;
   unsigned qsign = p.qsign;
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     const int vk = v_row_key(row);
     k_key[i] = row;
     v_key[i] = vk;
-    kgo[i] = (unsigned)((long long)row * tok + (pc ^ swz_k8<D>(row)) * 16);
-    vgo[i] = (unsigned)((long long)vk * tok + (pc ^ swz_v8<D>(row)) * 16);
+    kgo[i] = (unsigned)((long long)row * tkv + (pc ^ swz_k8<D>(row)) * 16);
+    vgo[i] = (unsigned)((long long)vk * tkv + (pc ^ swz_v8<D>(row)) * 16);
   }
   const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS unsigned char*)ks_base);
   const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS unsigned char*)vs_base);
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   auto load_tile = [&](const unsigned* go, const int* key, const unsigned char* src, unsigned lds_buf, int j) {
     const int kv0 = j * BC;
     const unsigned la0 = lds_buf + lds_wave;
-    const unsigned char* base = src + (long long)kv0 * tok;
+    const unsigned char* base = src + (long long)kv0 * tkv;
     if (kv0 + BC <= N) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     } else {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        const long long back = (long long)(kv0 + key[i] < N ? 0 : kv0 + key[i] - (N - 1)) * tok;
+        const long long back = (long long)(kv0 + key[i] < N ? 0 : kv0 + key[i] - (N - 1)) * tkv;
         const unsigned char* g = base + (long long)go[i] - back;
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
                      "v"(g)
@@ -400,7 +402,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   const float l_tot = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   if (myq < N) {
     const float sc = dv / l_tot;
-    __bf16* og = (__bf16*)p.o + head_base + (long long)myq * tok;
+    __bf16* og = (__bf16*)p.o + sv.q_base + (long long)myq * tok;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
       }
     }
     if (lh == 0) {
-      p.lse[(long long)bh * N + myq] =
+      p.lse[sv.lse_base + myq] =
           (m_ref - kPOffset + fast_log2(l_tot)) * 0.69314718055994531f;
     }
   }

@@ -30,12 +30,54 @@ struct FwdParams {
   const float* dq;   // fp8 only: per-(b,h) descales, device
   const float* dk;
   const float* dv;
-  int B, H, N;
-  int n_qtiles;      // ceil(N / rows per workgroup)
+  int B, H, N;       // N: sequence length (fixed-length calls)
+  int Hkv;           // K/V heads; query head h reads K/V head h / group
+  int group;         // H / Hkv
+  const int* cu;     // variable-length calls: device [B+1] token offsets, else null
+  int total;         // variable-length calls: tokens in the packed tensors
+  int maxlen;        // longest sequence (N for fixed-length calls)
+  int n_qtiles;      // ceil(maxlen / rows per workgroup)
   int remap;         // 1: XCD-aware block order (grid size divisible by 8)
   float c;           // |scale| * log2(e): scores are kept in log2 units
   unsigned qsign;    // sign-flip mask applied to Q when scale < 0
 };
+
+// The sequence one work-group works on: its length and the element offsets
+// of its first token in Q/O ([tokens][H][d]) and K/V ([tokens][Hkv][d]) and
+// of its first row in the log-sum-exp ([B][H][N], or [H][total] for
+// variable-length calls).
+struct SeqView {
+  int N;
+  int hk;            // K/V head
+  long long q_base, kv_base, lse_base;
+};
+
+// Fills `v` for (batch b, query head h) and returns false when the
+// work-group has nothing to do: its first query row q0 lies past the end of
+// the sequence, or the sequence's offsets are malformed (negative, not
+// increasing, past `total`, or longer than `maxlen`) -- such a sequence is
+// skipped and nothing outside the tensors is ever touched.
+__device__ __forceinline__ bool seq_view(const FwdParams& p, int D, int b, int h, int q0, SeqView& v) {
+  long long seq0;
+  int n;
+  if (p.cu) {
+    const int s0 = p.cu[b];
+    const int s1 = p.cu[b + 1];
+    if (s0 < 0 || s1 < s0 || s1 > p.total || s1 - s0 > p.maxlen) return false;
+    seq0 = s0;
+    n = s1 - s0;
+  } else {
+    seq0 = (long long)b * p.N;
+    n = p.N;
+  }
+  if (q0 >= n) return false;
+  v.N = n;
+  v.hk = h / p.group;
+  v.q_base = (seq0 * p.H + h) * D;
+  v.kv_base = (seq0 * p.Hkv + v.hk) * D;
+  v.lse_base = p.cu ? (long long)h * p.total + seq0 : ((long long)b * p.H + h) * n;
+  return true;
+}
 
 // Maps the launch index to (batch*head, query tile).  Work-groups are handed
 // to the 8 XCDs round-robin (block i -> XCD i % 8), so when the grid is a
@@ -43,9 +85,31 @@ struct FwdParams {
 // blocks -- the query tiles of one head, which share its K/V -- land on one
 // XCD and share its L2.  Within a head, tiles go longest-first (for causal
 // attention the last query tile sees the most keys).
+//
+// Variable-length calls order the work differently: sequence lengths vary,
+// so a contiguous run of heads per XCD would give one XCD all of a long
+// sequence.  Instead (batch, head) unit bh goes to XCD bh % 8 -- every XCD
+// gets the same share of every sequence and a head's K/V stay in one L2 --
+// and each XCD runs its units query-tile-major, last (longest) tiles first;
+// work-groups past the end of a short sequence exit at once.
 __device__ __forceinline__ void block_to_work(const FwdParams& p, int& bh, int& qt) {
   int total = gridDim.x;
   int L = blockIdx.x;
+  if (p.cu) {
+    const int BH = p.B * p.H;
+    if ((BH & 7) == 0) {
+      const int per = BH >> 3;
+      const int k = L >> 3;
+      const int t = k / per;
+      qt = p.n_qtiles - 1 - t;
+      bh = (L & 7) + 8 * (k - t * per);
+    } else {
+      const int t = L / BH;
+      qt = p.n_qtiles - 1 - t;
+      bh = L - t * BH;
+    }
+    return;
+  }
   if (p.remap) {
     int per = total >> 3;
     L = (L & 7) * per + (L >> 3);

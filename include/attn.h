@@ -55,8 +55,10 @@ extern "C" {
 
 /* Status codes returned by every entry point. */
 #define ATTN_OK 0
-#define ATTN_ERR_INVALID_ARG 1 /* null pointer, B/H/N <= 0, causal not 0/1, non-finite scale, size overflow */
-#define ATTN_ERR_UNSUPPORTED 2 /* head_dim not in {64, 128}, pointer not 16-byte aligned */
+#define ATTN_ERR_INVALID_ARG 1 /* null pointer, B/H/N <= 0, H not a multiple of H_kv, causal not 0/1,
+                                  non-finite scale, size overflow, inconsistent varlen sizes */
+#define ATTN_ERR_UNSUPPORTED 2 /* head_dim not in {64, 128}, pointer not 16-byte aligned (fp32 arrays:
+                                  4-byte), H * head_dim > 2^24, grid over 2^31 - 1 work-groups */
 #define ATTN_ERR_HIP 3         /* the HIP runtime reported an error at launch */
 
 /*
@@ -92,6 +94,72 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
                  const float* descale_q, const float* descale_k, const float* descale_v,
                  int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * Grouped-query and variable-length forms.  Grouped-query attention (GQA;
+ * MQA when H_kv = 1) lets several query heads share one key/value head, and
+ * variable-length batches pack sequences of different lengths without
+ * padding: "FlashAttention 4: Atenção Mais Rápida e Eficiente em Memória
+ * para LLMs", sections "Principais Conclusões" and "Compatibilidade e status
+ * atual", where both are listed as missing forward-pass features of the
+ * page's kernel.  The arithmetic is that of attn_fwd / attn_fwd_fp8; only
+ * which K/V rows a query row sees changes:
+ *   - query head h (0 <= h < H) reads K/V head h / (H / H_kv); H must be a
+ *     multiple of H_kv (H_kv = H is plain multi-head attention);
+ *   - in a variable-length batch every sequence is a separate attention
+ *     problem: its queries see only its own keys (and with causal = 1 only
+ *     keys 0..i of the same sequence for its query i).
+ *
+ * attn_fwd_gqa -- bf16, fixed length.
+ *   q, o   : bf16 [B][N][H][d];   k, v : bf16 [B][N][H_kv][d];
+ *   lse    : fp32 [B][H][N].  Other arguments as for attn_fwd.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int H_kv, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_varlen -- bf16, variable-length batch packed along the token axis.
+ *   q, o        : bf16 [total][H][d];   k, v : bf16 [total][H_kv][d];
+ *   lse         : fp32 [H][total] (row of query token t of head h at h*total + t);
+ *   cu_seqlens  : int32 [B+1], DEVICE, read by the kernel: sequence b owns
+ *                 token rows cu_seqlens[b] .. cu_seqlens[b+1]-1; the caller
+ *                 guarantees 0 = cu[0] <= cu[1] <= ... <= cu[B] = total and
+ *                 cu[b+1] - cu[b] <= max_seqlen.  A sequence whose offsets
+ *                 break this (negative, decreasing, past total, longer than
+ *                 max_seqlen) is skipped -- its rows of o and lse are not
+ *                 written -- and no memory outside the tensors is touched.
+ *                 Empty sequences are allowed.
+ *   B           : number of sequences, >= 1;
+ *   total       : token rows in the packed tensors, >= 0 (0: nothing is
+ *                 launched, the tensor pointers are not checked);
+ *   max_seqlen  : an upper bound on the sequence lengths, 1 <= max_seqlen <=
+ *                 total; the grid is sized from it.
+ *   H, H_kv, d, causal, scale, stream : as for attn_fwd_gqa.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int B, int total, int max_seqlen, int H, int H_kv,
+                    int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fwd_fp8_gqa -- OCP FP8 E4M3 form of attn_fwd_gqa.
+ *   q : e4m3fn [B][N][H][d];  k, v : e4m3fn [B][N][H_kv][d];  o : bf16; lse : fp32 [B][H][N].
+ *   descale_q : fp32 [B*H] (index b*H + h);
+ *   descale_k, descale_v : fp32 [B*H_kv] (index b*H_kv + hk), device.
+ */
+int attn_fwd_fp8_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const float* descale_q, const float* descale_k, const float* descale_v,
+                     int B, int H, int H_kv, int N, int d, int causal, float scale,
+                     hipStream_t stream);
+
+/*
+ * attn_fwd_fp8_varlen -- OCP FP8 E4M3 form of attn_fwd_varlen.
+ *   q : e4m3fn [total][H][d];  k, v : e4m3fn [total][H_kv][d];  o : bf16 [total][H][d];
+ *   lse : fp32 [H][total];  descales per (sequence b, head) as for attn_fwd_fp8_gqa.
+ */
+int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* descale_q, const float* descale_k, const float* descale_v,
+                        const int* cu_seqlens, int B, int total, int max_seqlen, int H, int H_kv,
+                        int d, int causal, float scale, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);

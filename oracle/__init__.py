@@ -19,12 +19,15 @@ tiled       the online-softmax recurrence over key/value tiles (running row
             untiled" exactness property and to count rescales.
 brute       a pure-Python (math.fsum) evaluation of the definition for tiny
             inputs, independent of NumPy.
+grouped     grouped-query (K/V heads shared by groups of query heads) and
+            variable-length (packed sequences) forms of the definition.
 """
 
 from .formats import bf16_bits_to_float64, e4m3fn_bits_to_float64, dequantize_e4m3
 from .attention import attention_forward, attention_head_rows
 from .tiled import tiled_online_softmax_head, simulator_counts
 from .brute import attention_brute
+from .grouped import attention_forward_gqa, attention_forward_varlen
 
 __all__ = [
     "bf16_bits_to_float64",
@@ -35,4 +38,6 @@ __all__ = [
     "tiled_online_softmax_head",
     "simulator_counts",
     "attention_brute",
+    "attention_forward_gqa",
+    "attention_forward_varlen",
 ]

@@ -31,7 +31,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_fp8", "attn_status_string", "attn_version"}
+    assert set(names) == {"attn_fwd", "attn_fwd_fp8", "attn_fwd_gqa", "attn_fwd_varlen",
+                          "attn_fwd_fp8_gqa", "attn_fwd_fp8_varlen", "attn_status_string",
+                          "attn_version"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -72,7 +74,42 @@ def call8(**kw):
                             check=False)
 
 
-@pytest.mark.parametrize("fn", [call, call8])
+def call_gqa(**kw):
+    a = dict(GOOD, Hkv=1)
+    a.update(kw)
+    return eat.attn_fwd_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"],
+                            a["N"], a["d"], a["causal"], a["scale"], None, check=False)
+
+
+def call8_gqa(**kw):
+    a = dict(GOOD, Hkv=1, dq=P + 0x5000, dk=P + 0x5100, dv=P + 0x5200)
+    a.update(kw)
+    return eat.attn_fwd_fp8_gqa(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"],
+                                a["dv"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                a["scale"], None, check=False)
+
+
+# variable-length calls: B sequences packed into N (= total) tokens
+def call_var(**kw):
+    a = dict(GOOD, Hkv=2, cu=P + 0x6000, maxlen=64)
+    a.update(kw)
+    return eat.attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["B"], a["N"],
+                               a["maxlen"], a["H"], a["Hkv"], a["d"], a["causal"], a["scale"],
+                               None, check=False)
+
+
+def call8_var(**kw):
+    a = dict(GOOD, Hkv=2, cu=P + 0x6000, maxlen=64, dq=P + 0x5000, dk=P + 0x5100, dv=P + 0x5200)
+    a.update(kw)
+    return eat.attn_fwd_fp8_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"],
+                                   a["dv"], a["cu"], a["B"], a["N"], a["maxlen"], a["H"], a["Hkv"],
+                                   a["d"], a["causal"], a["scale"], None, check=False)
+
+
+ALL_CALLS = [call, call8, call_gqa, call8_gqa, call_var, call8_var]
+
+
+@pytest.mark.parametrize("fn", ALL_CALLS)
 @pytest.mark.parametrize("kw,status", [
     (dict(q=0), eat.ATTN_ERR_INVALID_ARG),
     (dict(k=0), eat.ATTN_ERR_INVALID_ARG),
@@ -81,7 +118,7 @@ def call8(**kw):
     (dict(lse=0), eat.ATTN_ERR_INVALID_ARG),
     (dict(B=0), eat.ATTN_ERR_INVALID_ARG),
     (dict(H=-1), eat.ATTN_ERR_INVALID_ARG),
-    (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(N=-1), eat.ATTN_ERR_INVALID_ARG),
     (dict(causal=2), eat.ATTN_ERR_INVALID_ARG),
     (dict(causal=-1), eat.ATTN_ERR_INVALID_ARG),
     (dict(scale=math.inf), eat.ATTN_ERR_INVALID_ARG),
@@ -92,16 +129,54 @@ def call8(**kw):
     (dict(q=P + 8), eat.ATTN_ERR_UNSUPPORTED),
     (dict(o=P + 0x3002), eat.ATTN_ERR_UNSUPPORTED),
     (dict(lse=P + 0x4002), eat.ATTN_ERR_UNSUPPORTED),
-    (dict(B=1 << 30, N=1 << 30, H=1 << 30), eat.ATTN_ERR_INVALID_ARG),
-    (dict(B=65535, H=65535, N=1 << 20), eat.ATTN_ERR_UNSUPPORTED),   # grid beyond 2^31 blocks
+    (dict(H=1 << 18, d=128, Hkv=1), eat.ATTN_ERR_UNSUPPORTED),  # H*d beyond 2^24
 ])
 def test_invalid_arguments_rejected_on_host(lib, fn, kw, status):
     assert fn(**kw) == status
 
 
+@pytest.mark.parametrize("fn", [call, call8])
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=1 << 30, N=1 << 30, H=1 << 30), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=65535, H=65535, N=1 << 20), eat.ATTN_ERR_UNSUPPORTED),   # grid beyond 2^31 blocks
+])
+def test_fixed_length_sizes(lib, fn, kw, status):
+    assert fn(**kw) == status
+
+
+@pytest.mark.parametrize("fn", [call_gqa, call8_gqa, call_var, call8_var])
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hkv=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(Hkv=-2), eat.ATTN_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4), eat.ATTN_ERR_INVALID_ARG),    # H not a multiple of H_kv
+    (dict(H=2, Hkv=4), eat.ATTN_ERR_INVALID_ARG),
+])
+def test_kv_heads_checked(lib, fn, kw, status):
+    assert fn(**kw) == status
+
+
+@pytest.mark.parametrize("fn", [call_var, call8_var])
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(cu=P + 0x6002), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(B=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(N=-5), eat.ATTN_ERR_INVALID_ARG),           # total < 0
+    (dict(maxlen=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(maxlen=129), eat.ATTN_ERR_INVALID_ARG),     # longer than total (128)
+    (dict(N=1 << 30, maxlen=1 << 30, B=1 << 20, H=64, Hkv=64), eat.ATTN_ERR_UNSUPPORTED),  # grid
+    (dict(N=0, q=0, k=0, v=0, o=0, lse=0), eat.ATTN_OK),   # empty batch: nothing launched
+    (dict(N=0, H=3, Hkv=2), eat.ATTN_ERR_INVALID_ARG),
+    (dict(N=0, d=80), eat.ATTN_ERR_UNSUPPORTED),
+])
+def test_varlen_sizes(lib, fn, kw, status):
+    assert fn(**kw) == status
+
+
+@pytest.mark.parametrize("fn", [call8, call8_gqa, call8_var])
 @pytest.mark.parametrize("kw", [dict(dq=0), dict(dk=0), dict(dv=0)])
-def test_fp8_requires_descales(lib, kw):
-    assert call8(**kw) == eat.ATTN_ERR_INVALID_ARG
+def test_fp8_requires_descales(lib, fn, kw):
+    assert fn(**kw) == eat.ATTN_ERR_INVALID_ARG
 
 
 def test_binding_raises_with_status_name(lib):

@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_brute, attention_forward, attention_head_rows,
+from oracle import (attention_brute, attention_forward, attention_forward_gqa,
+                    attention_forward_varlen, attention_head_rows,
                     bf16_bits_to_float64, dequantize_e4m3, e4m3fn_bits_to_float64,
                     simulator_counts, tiled_online_softmax_head)
 
@@ -324,3 +325,115 @@ def test_dequantize_uses_per_batch_head_descale():
     for b in range(B):
         for h in range(H):
             assert np.all(x[b, :, h, :] == ds[b, h])
+
+
+# ---------------------------------------------------------------------------
+# grouped-query and variable-length forms
+# ---------------------------------------------------------------------------
+
+def _rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_with_all_heads_is_plain_attention(causal):
+    q, k, v = _rnd((2, 23, 4, 8), 1), _rnd((2, 23, 4, 8), 2), _rnd((2, 23, 4, 8), 3)
+    o1, l1 = attention_forward_gqa(q, k, v, 0.4, causal)
+    o2, l2 = attention_forward(q, k, v, 0.4, causal)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mqa_head_is_an_independent_single_head_problem(causal):
+    # one K/V head shared by every query head: head h alone, with that K/V,
+    # is a one-head problem of the (separately pinned) plain definition
+    q, k, v = _rnd((1, 19, 5, 8), 4), _rnd((1, 19, 1, 8), 5), _rnd((1, 19, 1, 8), 6)
+    o, lse = attention_forward_gqa(q, k, v, 0.3, causal)
+    for h in range(5):
+        oh, lh = attention_forward(q[:, :, h:h + 1], k, v, 0.3, causal)
+        assert np.allclose(o[:, :, h:h + 1], oh, rtol=0, atol=1e-15)
+        assert np.allclose(lse[:, h:h + 1], lh, rtol=0, atol=1e-15)
+
+
+def test_gqa_head_mapping_closed_form():
+    # K/V head j carries the constant value j + 1: every query row of query
+    # head h then averages constants, so it returns exactly the value of the
+    # K/V head it reads, h // (H / Hkv) + 1 (a modular mapping h % Hkv, or a
+    # swapped grouping, gives another number)
+    H, Hkv = 8, 2
+    q, k = _rnd((1, 9, H, 4), 7), _rnd((1, 9, Hkv, 4), 8)
+    v = np.broadcast_to(np.arange(1, Hkv + 1, dtype=np.float64)[None, None, :, None],
+                        (1, 9, Hkv, 4)).copy()
+    o, _ = attention_forward_gqa(q, k, v, 0.7, True)
+    for h in range(H):
+        assert np.allclose(o[0, :, h, :], h // (H // Hkv) + 1, rtol=0, atol=1e-14)
+
+
+def test_gqa_rejects_bad_head_counts():
+    with pytest.raises(ValueError):
+        attention_forward_gqa(_rnd((1, 4, 6, 4), 1), _rnd((1, 4, 4, 4), 2), _rnd((1, 4, 4, 4), 3),
+                              1.0, False)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_of_equal_lengths_is_the_fixed_length_batch(causal):
+    B, N, H, Hkv, d = 3, 11, 4, 2, 8
+    q, k, v = _rnd((B, N, H, d), 9), _rnd((B, N, Hkv, d), 10), _rnd((B, N, Hkv, d), 11)
+    cu = np.arange(B + 1) * N
+    o, lse = attention_forward_varlen(q.reshape(B * N, H, d), k.reshape(B * N, Hkv, d),
+                                      v.reshape(B * N, Hkv, d), cu, 0.5, causal)
+    o2, l2 = attention_forward_gqa(q, k, v, 0.5, causal)
+    assert np.allclose(o.reshape(B, N, H, d), o2, rtol=0, atol=1e-15)
+    # lse [H][total] against [B][H][N]
+    assert np.allclose(lse.reshape(H, B, N).transpose(1, 0, 2), l2, rtol=0, atol=1e-15)
+
+
+def test_varlen_sequences_do_not_see_each_other():
+    # a sequence's output is unchanged when the other sequences' keys and
+    # values are replaced; each one equals its own one-sequence problem
+    lengths = [5, 1, 0, 9]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, Hkv, d = cu[-1], 2, 1, 4
+    q, k, v = _rnd((T, H, d), 12), _rnd((T, Hkv, d), 13), _rnd((T, Hkv, d), 14)
+    o, lse = attention_forward_varlen(q, k, v, cu, 0.8, False)
+    k2, v2 = k.copy(), v.copy()
+    k2[cu[3]:], v2[cu[3]:] = 100.0, -100.0        # alter the last sequence only
+    o2, l2 = attention_forward_varlen(q, k2, v2, cu, 0.8, False)
+    assert np.array_equal(o[:cu[3]], o2[:cu[3]]) and np.array_equal(lse[:, :cu[3]], l2[:, :cu[3]])
+    for b in range(len(lengths)):
+        s0, s1 = cu[b], cu[b + 1]
+        if s1 == s0:
+            continue
+        ob, lb = attention_forward_gqa(q[None, s0:s1], k[None, s0:s1], v[None, s0:s1], 0.8, False)
+        assert np.allclose(o[s0:s1], ob[0], rtol=0, atol=1e-15)
+        assert np.allclose(lse[:, s0:s1], lb[0], rtol=0, atol=1e-15)
+
+
+def test_varlen_causal_first_token_of_each_sequence():
+    # causal: the first query of every sequence sees only its own first key,
+    # so its output is that key's value row and its lse the single score
+    lengths = [3, 1, 6]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, d = cu[-1], 2, 4
+    q, k, v = _rnd((T, H, d), 15), _rnd((T, H, d), 16), _rnd((T, H, d), 17)
+    o, lse = attention_forward_varlen(q, k, v, cu, 0.6, True)
+    for b in range(len(lengths)):
+        t = cu[b]
+        assert np.allclose(o[t], v[t], rtol=0, atol=1e-15)
+        for h in range(H):
+            assert math.isclose(lse[h, t], 0.6 * float(q[t, h] @ k[t, h]), abs_tol=1e-14)
+
+
+def test_varlen_row_sample_matches_full():
+    lengths = [7, 0, 12]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, d = cu[-1], 3, 4
+    q, k, v = _rnd((T, H, d), 18), _rnd((T, 1, d), 19), _rnd((T, 1, d), 20)
+    o, lse = attention_forward_varlen(q, k, v, cu, 0.5, True)
+    rows = [np.tile(np.array([n - 1, 0][:min(n, 2)]), (H, 1)) for n in lengths]
+    os_, ls_ = attention_forward_varlen(q, k, v, cu, 0.5, True, rows=rows)
+    for b, n in enumerate(lengths):
+        for h in range(H):
+            for i, r in enumerate(rows[b][h]):
+                assert np.array_equal(os_[b][h, i], o[cu[b] + r, h])
+                assert ls_[b][h, i] == lse[h, cu[b] + r]

@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 from oracle import bf16_bits_to_float64, dequantize_e4m3
-from workloads import WORKLOADS, Workload, make_bf16, make_fp8, sample_rows
+from workloads import WORKLOADS, Workload, make_bf16, make_fp8, sample_rows, make_inputs
 
 
 def test_bf16_inputs_are_seeded_and_shaped():
@@ -62,3 +62,32 @@ def test_row_sample_includes_ends_and_is_distinct():
     np.testing.assert_array_equal(r, sample_rows(w))
     small = sample_rows(WORKLOADS["tiny"])
     assert small.shape == (1, 2, 128)
+
+
+def test_grouped_query_shapes():
+    w = Workload("g", 95, 2, 8, 40, 64, "bf16", (True,), Hkv=2)
+    x = make_inputs(w)
+    assert x["q"].shape == (2, 40, 8, 64)
+    assert x["k"].shape == x["v"].shape == (2, 40, 2, 64)
+    w8 = Workload("g8", 96, 2, 8, 40, 64, "fp8", (False,), Hkv=4, outliers=True)
+    x8 = make_inputs(w8)
+    assert x8["dq"].shape == (2, 8) and x8["dk"].shape == (2, 4) and x8["dv"].shape == (2, 4)
+
+
+def test_varlen_layout_and_offsets():
+    w = WORKLOADS["varlen"]
+    assert w.lengths[0] == 8192 and w.lengths[1] == 1 and len(w.lengths) == w.B
+    assert all(1 <= n <= 8192 for n in w.lengths) and w.N == max(w.lengths)
+    assert w.flops(True) == sum(2.0 * w.H * n * n * w.d for n in w.lengths)
+    small = Workload("v", 97, 3, 4, 9, 64, "fp8", (False,), Hkv=2, lengths=(9, 0, 4),
+                     outliers=True)
+    x = make_inputs(small)
+    assert list(x["cu"]) == [0, 9, 9, 13]
+    assert x["q"].shape == (1, 13, 4, 64) and x["k"].shape == (1, 13, 2, 64)
+    assert x["dq"].shape == (3, 4) and x["dk"].shape == (3, 2)
+    # per-sequence descale: every sequence's largest code magnitude is the
+    # e4m3 maximum (448 = code 0x7e with the sign bit cleared)
+    for b, (s0, s1) in enumerate([(0, 9), (9, 9), (9, 13)]):
+        if s1 > s0:
+            for h in range(4):
+                assert (x["q"][0, s0:s1, h] & 0x7F).max() == 0x7E

@@ -13,7 +13,14 @@ Workloads (shape B, H, N, d; data; mode):
   ctx32k    1, 32, 32768, 128  bf16 N(0,1), 1% of K rows x8     causal
   fp8_8k    2, 16, 8192, 128   OCP e4m3 from N(0,1) with 0.1%
                                outliers x20, per-(b,h) descale  non-causal
-The scale is 1/sqrt(d) everywhere.
+  gqa8k     2, 32/8, 8192, 128 bf16 N(0,1); 32 query heads over
+                               8 K/V heads                      causal
+  varlen    8 sequences, 16/4 heads, d 128, bf16 N(0,1); packed
+            lengths drawn in [2, 8192] with the first fixed at
+            8192 and the second at 1 (about 33k tokens)         causal
+The scale is 1/sqrt(d) everywhere.  Grouped-query workloads give K and V
+Hkv heads ([B][N][Hkv][d]); variable-length workloads pack their sequences
+along the token axis ([total][heads][d], offsets in "cu").
 
 Recipe (all draws on the CPU with torch.Generator, so the same seed gives the
 same bytes on every machine running this torch build):
@@ -50,15 +57,42 @@ class Workload:
     modes: tuple          # causal flags to run
     peaked_k: bool = False
     outliers: bool = False
+    Hkv: int = 0          # K/V heads; 0: same as H
+    lengths: tuple = ()   # variable-length batch: the sequence lengths (B = len, N = max)
 
     @property
     def scale(self):
         return 1.0 / math.sqrt(self.d)
 
+    @property
+    def kv_heads(self):
+        return self.Hkv or self.H
+
+    @property
+    def varlen(self):
+        return bool(self.lengths)
+
+    @property
+    def total(self):
+        return sum(self.lengths) if self.lengths else self.B * self.N
+
     def flops(self, causal):
-        """4*B*H*N^2*d, halved when causal (the metric's convention)."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        """4*B*H*N^2*d, halved when causal (the metric's convention); for a
+        variable-length batch the sum of 4*H*n^2*d over its sequences."""
+        if self.lengths:
+            f = sum(4.0 * self.H * n * n * self.d for n in self.lengths)
+        else:
+            f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if causal else f
+
+
+def varlen_lengths(wid, count, max_len):
+    """Seeded sequence lengths for a variable-length workload: the first is
+    max_len, the second 1, the rest uniform in [2, max_len]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(1000 * wid + 6)
+    rest = torch.randint(2, max_len + 1, (count - 2,), generator=g).tolist()
+    return tuple([max_len, 1] + rest)
 
 
 WORKLOADS = {
@@ -68,7 +102,11 @@ WORKLOADS = {
     "long8k64": Workload("long8k64", 6, 2, 32, 8192, 64, "bf16", (True,)),
     "ctx32k": Workload("ctx32k", 4, 1, 32, 32768, 128, "bf16", (True,), peaked_k=True),
     "fp8_8k": Workload("fp8_8k", 5, 2, 16, 8192, 128, "fp8", (False,), outliers=True),
+    "gqa8k": Workload("gqa8k", 7, 2, 32, 8192, 128, "bf16", (True,), Hkv=8),
 }
+_VL = varlen_lengths(8, 8, 8192)
+WORKLOADS["varlen"] = Workload("varlen", 8, len(_VL), 16, max(_VL), 128, "bf16", (True,), Hkv=4,
+                               lengths=_VL)
 
 SAMPLE_ROWS = 512
 E4M3_MAX = 448.0
@@ -104,39 +142,84 @@ def bf16_bits(t):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
-def make_bf16(w, shape=None):
-    """Q, K, V for a bf16 workload as uint16 bf16 bit arrays [B][N][H][d]."""
+def cu_seqlens(lengths):
+    """int32 offsets [B+1] of packed sequences."""
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+
+def _shapes(w, shape):
+    """(B, N, H, d) and the per-tensor array shapes: [B][N][heads][d], or
+    [1][total][heads][d] for a variable-length workload."""
     B, N, H, d = shape if shape is not None else (w.B, w.N, w.H, w.d)
+    Hkv = w.Hkv or H
+    if w.lengths:
+        T = sum(w.lengths)
+        return (B, N, H, d), {"q": (1, T, H, d), "k": (1, T, Hkv, d), "v": (1, T, Hkv, d)}
+    return (B, N, H, d), {"q": (B, N, H, d), "k": (B, N, Hkv, d), "v": (B, N, Hkv, d)}
+
+
+def _peak_rows(w, x, N):
+    """Multiplies round(0.01 N) distinct key rows of every (b, K/V head) by 8."""
+    Bx, _, Hx, _ = x.shape
+    npk = int(round(0.01 * N))
+    for b in range(Bx):
+        for h in range(Hx):
+            rows = _perm_prefix(N, npk, seed_for(w.wid, 3) * 7919 + b * Hx + h)
+            x[b, rows, h, :] *= 8.0
+
+
+def make_bf16(w, shape=None):
+    """Q, K, V for a bf16 workload as uint16 bf16 bit arrays (shapes as in
+    ``_shapes``), plus "cu" offsets for a variable-length workload."""
+    (B, N, H, d), shp = _shapes(w, shape)
     out = {}
     for tid, name in enumerate(("q", "k", "v")):
-        x = _randn((B, N, H, d), seed_for(w.wid, tid))
+        x = _randn(shp[name], seed_for(w.wid, tid))
         if name == "k" and w.peaked_k:
-            npk = int(round(0.01 * N))
-            for b in range(B):
-                for h in range(H):
-                    rows = _perm_prefix(N, npk, seed_for(w.wid, 3) * 7919 + b * H + h)
-                    x[b, rows, h, :] *= 8.0
+            _peak_rows(w, x, N)
         out[name] = bf16_bits(x)
+    if w.lengths:
+        out["cu"] = cu_seqlens(w.lengths)
     return out
 
 
+def _quantize(x, descale_of):
+    y = (x / descale_of).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def make_fp8(w, shape=None):
-    """Q, K, V for an fp8 workload: uint8 e4m3fn codes [B][N][H][d] and
-    float32 descales [B][H] per tensor."""
-    B, N, H, d = shape if shape is not None else (w.B, w.N, w.H, w.d)
+    """Q, K, V for an fp8 workload: uint8 e4m3fn codes (shapes as in
+    ``_shapes``) and float32 descales [B][heads] per tensor (per sequence for
+    a variable-length workload), plus "cu" offsets when variable-length."""
+    (B, N, H, d), shp = _shapes(w, shape)
     out = {}
     for tid, name in enumerate(("q", "k", "v")):
-        x = _randn((B, N, H, d), seed_for(w.wid, tid))
+        x = _randn(shp[name], seed_for(w.wid, tid))
         if w.outliers:
             n_out = int(round(0.001 * x.numel()))
             idx = _perm_prefix(x.numel(), n_out, seed_for(w.wid, 4) + 10 * tid)
             flat = x.view(-1)
             flat[idx] *= 20.0
-        amax = x.abs().amax(dim=(1, 3))                       # [B][H]
-        descale = torch.clamp(amax, min=1e-30) / E4M3_MAX
-        y = (x / descale[:, None, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
-        out[name] = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-        out["d" + name] = descale.to(torch.float32).numpy()
+        if w.lengths:
+            cu = cu_seqlens(w.lengths)
+            nh = x.shape[2]
+            descale = torch.empty((len(w.lengths), nh), dtype=torch.float32)
+            codes = np.empty(x.shape, dtype=np.uint8)
+            for b in range(len(w.lengths)):
+                seg = x[:, cu[b]:cu[b + 1]]
+                amax = seg.abs().amax(dim=(0, 1, 3)) if seg.shape[1] else torch.zeros(nh)
+                descale[b] = torch.clamp(amax, min=1e-30) / E4M3_MAX
+                codes[:, cu[b]:cu[b + 1]] = _quantize(seg, descale[b][None, None, :, None])
+            out[name] = codes
+            out["d" + name] = descale.numpy()
+        else:
+            amax = x.abs().amax(dim=(1, 3))                       # [B][heads]
+            descale = torch.clamp(amax, min=1e-30) / E4M3_MAX
+            out[name] = _quantize(x, descale[:, None, :, None])
+            out["d" + name] = descale.to(torch.float32).numpy()
+    if w.lengths:
+        out["cu"] = cu_seqlens(w.lengths)
     return out
 
 
