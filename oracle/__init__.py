@@ -21,6 +21,8 @@ brute       a pure-Python (math.fsum) evaluation of the definition for tiny
             inputs, independent of NumPy.
 grouped     grouped-query (K/V heads shared by groups of query heads) and
             variable-length (packed sequences) forms of the definition.
+backward    the gradients dQ, dK, dV of the definition (chain rule), and the
+            row quantity D = sum(dO * O).
 """
 
 from .formats import bf16_bits_to_float64, e4m3fn_bits_to_float64, dequantize_e4m3
@@ -28,6 +30,7 @@ from .attention import attention_forward, attention_head_rows
 from .tiled import tiled_online_softmax_head, simulator_counts
 from .brute import attention_brute
 from .grouped import attention_forward_gqa, attention_forward_varlen
+from .backward import attention_backward, attention_backward_head, attention_delta
 
 __all__ = [
     "bf16_bits_to_float64",
@@ -40,4 +43,7 @@ __all__ = [
     "attention_brute",
     "attention_forward_gqa",
     "attention_forward_varlen",
+    "attention_backward",
+    "attention_backward_head",
+    "attention_delta",
 ]

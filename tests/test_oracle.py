@@ -18,7 +18,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_brute, attention_forward, attention_forward_gqa,
+from oracle import (attention_backward, attention_brute, attention_delta, attention_forward,
+                    attention_forward_gqa,
                     attention_forward_varlen, attention_head_rows,
                     bf16_bits_to_float64, dequantize_e4m3, e4m3fn_bits_to_float64,
                     simulator_counts, tiled_online_softmax_head)
@@ -437,3 +438,68 @@ def test_varlen_row_sample_matches_full():
             for i, r in enumerate(rows[b][h]):
                 assert np.array_equal(os_[b][h, i], o[cu[b] + r, h])
                 assert ls_[b][h, i] == lse[h, cu[b] + r]
+
+
+# ---------------------------------------------------------------------------
+# gradients
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, v, do, scale, causal):
+    o, _ = attention_forward(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_match_central_differences_of_the_forward(causal):
+    # L = sum(dO * O(q, k, v)): the analytic gradients against numerical
+    # derivatives of the separately pinned forward definition
+    B, N, H, d, scale = 1, 6, 2, 4, 0.7
+    q, k, v, do = (_rnd((B, N, H, d), s) for s in (21, 22, 23, 24))
+    dq, dk, dv = attention_backward(q, k, v, do, scale, causal)
+    eps = 1e-6
+    rng = np.random.default_rng(25)
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(12):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num = (_loss(args_p["q"], args_p["k"], args_p["v"], do, scale, causal) -
+                   _loss(args_m["q"], args_m["k"], args_m["v"], do, scale, causal)) / (2 * eps)
+            assert math.isclose(g[idx], num, rel_tol=1e-6, abs_tol=1e-8), (name, idx, g[idx], num)
+
+
+def test_zero_upstream_gradient_gives_zero_gradients():
+    q, k, v = (_rnd((1, 5, 1, 4), s) for s in (26, 27, 28))
+    for g in attention_backward(q, k, v, np.zeros_like(q), 0.5, True):
+        assert np.array_equal(g, np.zeros_like(g))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_gradients_sum_to_zero_and_value_gradients_sum_to_dout(causal):
+    # softmax is unchanged when every key of a head moves by one vector, so
+    # the key gradients of a head sum to zero; each softmax row sums to 1,
+    # so the value gradients of a head sum to the sum of the dO rows
+    q, k, v, do = (_rnd((2, 9, 3, 5), s) for s in (29, 30, 31, 32))
+    dq, dk, dv = attention_backward(q, k, v, do, 0.6, causal)
+    assert np.allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    assert np.allclose(dv.sum(axis=1), do.sum(axis=1), atol=1e-12)
+
+
+def test_causal_first_query_has_zero_gradient():
+    q, k, v, do = (_rnd((1, 7, 2, 4), s) for s in (33, 34, 35, 36))
+    dq, _, _ = attention_backward(q, k, v, do, 0.9, True)
+    assert np.allclose(dq[:, 0], 0.0, atol=1e-15)
+
+
+def test_delta_is_rowsum_of_p_times_dp():
+    q, k, v, do = (_rnd((1, 8, 1, 4), s) for s in (37, 38, 39, 40))
+    o, _ = attention_forward(q, k, v, 0.5, False)
+    s = 0.5 * q[0, :, 0] @ k[0, :, 0].T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    dp = do[0, :, 0] @ v[0, :, 0].T
+    assert np.allclose(attention_delta(o, do)[0, 0], (p * dp).sum(axis=1), atol=1e-13)
