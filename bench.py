@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz dense MFMA
 METRIC = "attn fwd TFLOPS (4BHN²d, causal halved) + % of MI355X MFMA peak, 1 GPU"
+METRIC_BWD = "attn bwd TFLOPS (2.5 x 4BHN²d, causal halved) + % of MI355X MFMA peak, 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -160,6 +161,8 @@ def main():
     ap.add_argument("--workload", default="long8k")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
+                    help="time the forward (default) or the backward pass (bf16 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -223,6 +226,20 @@ def main():
 
     o = torch.empty((T, w.H, w.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.H, T) if w.varlen else (w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    if args.which == "bwd":
+        if w.dtype != "bf16" or w.varlen or Hkv != w.H:
+            print("--pass bwd takes a bf16 multi-head workload", file=sys.stderr)
+            sys.exit(2)
+        from workloads import make_dout
+        step()                                     # O and lse of the forward
+        torch.cuda.synchronize()
+        do = dev16(make_dout(w))
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            eat.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, w.B, w.H, w.N, w.d, int(causal),
+                         w.scale, stream)
 
     for _ in range(args.warmup):
         step()
@@ -254,16 +271,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    if not bool(torch.isfinite(lse).all()) or not bool(torch.isfinite(o.float()).all()):
+    outs = [lse, o] + ([dq, dk, dv] if args.which == "bwd" else [])
+    if not all(bool(torch.isfinite(x.float()).all()) for x in outs):
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
 
-    flops = w.flops(causal)
+    flops = w.flops(causal) * (2.5 if args.which == "bwd" else 1.0)
     peak = PEAK_TFLOPS[w.dtype]
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -285,7 +303,10 @@ def main():
                      "traffic": measured_traffic(w.name, w.dtype, causal),
                      "kernel_avg_ms": round(avg_launch_ms, 4)},
     }
-    if not args.no_cpu_baseline:
+    if args.which == "bwd":
+        out["config"]["pass"] = "bwd"
+        out["roofline"]["traffic"] = None
+    if not args.no_cpu_baseline and args.which == "fwd":
         out["cpu_baseline"] = cpu_baseline(w, inp, causal)
     print(json.dumps(out), flush=True)
 

@@ -58,6 +58,8 @@ def load_library():
     lib.attn_fwd_fp8_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                         f, vp]
     lib.attn_fwd_fp8_varlen.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_bwd.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -157,4 +159,16 @@ def attn_fwd_fp8_varlen(q, k, v, o, lse, descale_q, descale_k, descale_v, cu_seq
                                             _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_fwd_fp8_varlen")
+    return st
+
+
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, stream=None,
+             check=True):
+    """bf16 backward; see attn_bwd in include/attn.h (``delta`` is a device
+    fp32 [B][H][N] workspace)."""
+    st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), int(B), int(H),
+                                 int(N), int(d), int(causal), float(scale), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_bwd")
     return st

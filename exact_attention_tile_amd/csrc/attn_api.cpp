@@ -16,6 +16,10 @@ int bf16_rows_per_block(int d);
 hipError_t launch_bf16(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream);
 int fp8_rows_per_block(int d);
 hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream);
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* delta, int B, int H, int N, int d, int causal, float scale,
+                           hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -216,6 +220,26 @@ extern "C" int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, 
   prm.dk = descale_k;
   prm.dv = descale_v;
   return run_fp8(prm, d, causal, scale, stream);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        float* delta, int B, int H, int N, int d, int causal, float scale,
+                        hipStream_t stream) {
+  int64_t tokens = 0;
+  int st = validate_fixed(B, N, &tokens);
+  if (st != ATTN_OK) return st;
+  st = validate(q, k, v, o, lse, tokens, H, H, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  if (!dout || !dq || !dk || !dv || !delta) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_UNSUPPORTED;
+  if (((uintptr_t)delta & 3u) != 0) return ATTN_ERR_UNSUPPORTED;
+  const int64_t grid = (int64_t)B * H * ((N + 127) / 128);   // the larger of the kernels' grids
+  if (grid > INT32_MAX || (tokens * H + 15) / 16 > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  const hipError_t e = attn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N,
+                                             d, causal, scale, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 extern "C" const char* attn_status_string(int status) {

@@ -1,0 +1,586 @@
+// bf16 backward of the tiled exact attention for gfx950 (MI355X, CDNA4).
+//
+// Gradients of O = softmax(Q K^T * scale) V with respect to Q, K and V (the
+// backward pass that "FlashAttention 4: Atenção Mais Rápida e Eficiente em
+// Memória para LLMs", section "Principais Conclusões", and "FlashAttention-4
+// no Blackwell B200 ...", section "Redução de tráfego no backward", name as
+// the forward kernel's counterpart), by the chain rule on the definition:
+//   P = softmax(scale Q K^T)  (recomputed tile by tile from the forward's
+//                              log-sum-exp: P = exp2(scale log2(e) S - lse log2(e)))
+//   dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+//   dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
+// Like the forward, the N x N matrices P, dP, dS never reach HBM.
+//
+// Three kernels (four at d = 128), enqueued in order on the caller's stream:
+//   delta : D_i for every row (a dot product of two rows), into the caller's
+//           fp32 workspace [B][H][N];
+//   dQ    : one work-group per (batch, head, 256 queries); each wave owns 32
+//           query columns and streams 64-key K/V tiles through LDS:
+//             S^T = K Q^T, dP^T = V dO^T (A = K / V rows, B = Q^T / dO^T in
+//             VGPRs), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (A = K^T from
+//             transposing LDS reads, B = dS^T packed to bf16);
+//   dK/dV : one work-group per (batch, head, 256 keys); each wave owns 32
+//           key columns (its K and V rows in registers; at d = 128 dV and dK
+//           come from two kernels, see below) and streams 64-query Q / dO
+//           tiles (plus their lse and D values) through LDS:
+//             S = Q K^T, dP = dO V^T (A = Q / dO rows), dS = P (dP - D),
+//             dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T from transposing
+//             LDS reads, B = P / dS packed to bf16).
+// No atomics: each output element is produced by exactly one lane, so the
+// results are deterministic.  The lane ownership, the 32x32x16 bf16 MFMA
+// layouts and the key/query permutation of the packed operands are those of
+// the forward kernel (attn_fwd_bf16.hip); masked entries get P = 0 after the
+// exponential, so the scale may have either sign.
+#include "attn_kernels.hpp"
+
+namespace attn {
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;
+  int B, H, N;
+  int n_tiles;       // ceil(N / 256): query tiles per head (dQ)
+  int n_ktiles;      // ceil(N / 256): key tiles per head (dK/dV)
+  float c;           // scale * log2(e)
+  float scale;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 16-byte-chunk XOR swizzle of the row-major [rows][D] LDS tiles: a
+// ds_read_b128 of 16 lanes on 16 consecutive rows at one chunk hits
+// distinct banks.  The transposing reads of the same tiles see at most a
+// 2-way conflict.
+template <int D> __device__ __forceinline__ int swz_b(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) {
+  return __uint_as_float((unsigned)b << 16);
+}
+
+// ---------------------------------------------------------------------------
+// delta: D[b][h][n] = sum_c dO[b][n][h][c] O[b][n][h][c]; 16 lanes per row
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
+  constexpr int LPR = 16;                 // lanes per row
+  constexpr int EPL = D / LPR;            // elements per lane (8 or 4)
+  const long long rows = (long long)p.B * p.N * p.H;
+  const long long row = (long long)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  const int sub = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const unsigned short* o = (const unsigned short*)p.o + row * D + sub * EPL;
+    const unsigned short* g = (const unsigned short*)p.dout + row * D + sub * EPL;
+    unsigned short ob[EPL], gb[EPL];
+    if constexpr (EPL == 8) {
+      *(u32x4*)ob = *(const u32x4*)o;
+      *(u32x4*)gb = *(const u32x4*)g;
+    } else {
+      *(u32x2*)ob = *(const u32x2*)o;
+      *(u32x2*)gb = *(const u32x2*)g;
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc = __builtin_fmaf(bf16_to_f32(ob[e]), bf16_to_f32(gb[e]), acc);
+  }
+  acc += __shfl_xor(acc, 8, LPR);
+  acc += __shfl_xor(acc, 4, LPR);
+  acc += __shfl_xor(acc, 2, LPR);
+  acc += __shfl_xor(acc, 1, LPR);
+  if (sub == 0 && row < rows) {
+    const long long nh = (long long)p.N * p.H;
+    const long long b = row / nh;
+    const long long rem = row - b * nh;
+    const long long n = rem / p.H;
+    const long long h = rem - n * p.H;
+    p.delta[(b * p.H + h) * p.N + n] = acc;
+  }
+}
+
+// Tile loader shared by the dQ and dK/dV kernels: the NW waves of a
+// work-group each fill LPW 1 KiB pieces of a [64][D] bf16 tile with
+// global_load_lds_dwordx4 (lane l fills bytes [16 l, 16 l + 16) after the
+// wave-uniform base in M0), choosing each lane's source chunk so that the
+// tile lands swizzled; rows past N are clamped to row N-1.
+template <int D, int NW>
+struct TileLoader {
+  static constexpr int TILE = 64 * D;
+  static constexpr int LPW = TILE * 2 / 1024 / NW;
+  static_assert(LPW >= 1 && LPW * 1024 * NW == TILE * 2, "tile must split into 1 KiB per load");
+  int row[LPW];
+  unsigned go[LPW];
+  unsigned lds_wave;
+  __device__ void init(int wave, int lane, long long tok) {
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int off = (wave * LPW + i) * 512 + lane * 8;   // element offset in the tile
+      const int r = off / D;
+      const int pc = (off - r * D) / 8;
+      row[i] = r;
+      go[i] = (unsigned)(((long long)r * tok + (pc ^ swz_b<D>(r)) * 8) * 2);
+    }
+    lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wave * LPW * 1024));
+  }
+  // rows row0 .. row0+63 of the tensor at src (element (row, 0) = src + row*tok)
+  __device__ void load(const __bf16* src, long long tok, unsigned lds_buf, int row0, int N) const {
+    const unsigned la0 = lds_buf + lds_wave;
+    const __bf16* base = src + (long long)row0 * tok;
+    if (row0 + 64 <= N) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i)
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
+                     "v"(go[i]), "s"(base)
+                     : "memory");
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const long long back = (long long)(row0 + row[i] < N ? 0 : row0 + row[i] - (N - 1)) * tok;
+        const __bf16* g = base + (long long)(go[i] / 2) - back;
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
+                     "v"(g)
+                     : "memory");
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Per-lane element offsets of the transposing reads of a swizzled [rows][D]
+// tile that give a lane (m = ln of a 32-wide column block db, h = lh) the
+// 8 rows 4h + (t&3) + 8(t>>2) (t = 0..7) of a 16-row group: the low 4 rows
+// from `lo`, the high 4 from `hi` (the swizzle differs between them).
+template <int D, int NDB>
+struct TrOffsets {
+  int lo[NDB], hi[NDB];
+  __device__ void init(int lane) {
+    const int gi = lane & 15;
+    const int lh = lane >> 5;
+    const int r_lo = 4 * lh + (gi >> 2);
+    const int r_hi = r_lo + 8;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int chunk = 4 * db + ((lane & 16) >> 3) + ((gi & 3) >> 1);
+      lo[db] = r_lo * D + ((chunk ^ swz_b<D>(r_lo)) * 8) + (gi & 1) * 4;
+      hi[db] = r_hi * D + ((chunk ^ swz_b<D>(r_hi)) * 8) + (gi & 1) * 4;
+    }
+  }
+};
+
+// A operand from two transposing reads (rows 16-row group at `base`)
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16* base, int lo, int hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(base + hi));
+  const u32x2 a2 = __builtin_bit_cast(u32x2, a);
+  const u32x2 b2 = __builtin_bit_cast(u32x2, b);
+  u32x4 w;
+  w[0] = a2[0];
+  w[1] = a2[1];
+  w[2] = b2[0];
+  w[3] = b2[1];
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+// bf16 [row][D] store of a 32x32 accumulator block set (lane owns row `row`,
+// register 4g+x of block db holds column 32 db + 8 g + 4 lh + x), scaled
+template <int NDB>
+__device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[NDB], float s, int lh) {
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = db * 32 + 8 * g + 4 * lh;
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * g + 0] * s, acc[db][4 * g + 1] * s);
+      w[1] = pack_bf16x2(acc[db][4 * g + 2] * s, acc[db][4 * g + 3] * s);
+      *(u32x2*)(dst + d0) = w;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: per (batch, head, 256 query rows); 64-key K/V tiles
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int BR = 256, BC = 64;
+  constexpr int NKB = BC / 32, NKK = BC / 16, NKS = D / 16, NDB = D / 32;
+  constexpr int TILE = BC * D;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];
+  __bf16* ks_base = smem;
+  __bf16* vs_base = smem + 2 * TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+
+  const int bh = blockIdx.x / p.n_tiles;
+  const int qt = p.n_tiles - 1 - (blockIdx.x - bh * p.n_tiles);   // longest first
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int N = p.N;
+  const long long tok = (long long)p.H * D;
+  const long long head_base = ((long long)b * N * p.H + h) * D;
+  const int q0 = qt * BR;
+  const int qw0 = q0 + wave * 32;
+  const int myq = qw0 + ln;
+  const int qr = myq < N ? myq : N - 1;
+
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
+  const __bf16* __restrict__ gg = (const __bf16*)p.dout + head_base;
+
+  // Q^T and dO^T fragments (B operands): lane (n = ln, h = lh) holds row
+  // myq, columns 16 ks + 8 lh .. +7
+  bf16x8 qf[NKS], gf[NKS];
+  {
+    const u32x4* qs = (const u32x4*)(qg + (long long)qr * tok + 8 * lh);
+    const u32x4* gs = (const u32x4*)(gg + (long long)qr * tok + 8 * lh);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = __builtin_bit_cast(bf16x8, qs[2 * ks]);
+      gf[ks] = __builtin_bit_cast(bf16x8, gs[2 * ks]);
+    }
+  }
+  const float lse2 = p.lse[(long long)bh * N + qr] * kLog2e;
+  const float dd = p.delta[(long long)bh * N + qr];
+  const float c = p.c;
+
+  const int n_kv_all = (N + BC - 1) / BC;
+  int wg_tiles = n_kv_all;
+  int wv_tiles = qw0 < N ? n_kv_all : 0;
+  if (CAUSAL) {
+    wg_tiles = min(q0 + BR - 1, N - 1) / BC + 1;
+    if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
+  }
+
+  TileLoader<D, 8> ld;
+  ld.init(wave, lane, tok);
+  const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS __bf16*)ks_base);
+  const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS __bf16*)vs_base);
+
+  int koff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = ln * D + (((2 * ks + lh) ^ swz_b<D>(ln)) * 8);
+  TrOffsets<D, NDB> tro;
+  tro.init(lane);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+  if (wg_tiles > 0) {
+    ld.load(kg, tok, lds_k, 0, N);
+    ld.load(vg, tok, lds_v, 0, N);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = 0; j < wg_tiles; ++j) {
+    if (j + 1 < wg_tiles) {
+      const unsigned nb = (unsigned)(((j + 1) & 1) * TILE * 2);
+      ld.load(kg, tok, lds_k + nb, (j + 1) * BC, N);
+      ld.load(vg, tok, lds_v + nb, (j + 1) * BC, N);
+    }
+    if (j < wv_tiles) {
+      const __bf16* kt = ks_base + (j & 1) * TILE;
+      const __bf16* vt = vs_base + (j & 1) * TILE;
+      const int kv0 = j * BC;
+      f32x16 s[NKB], dp[NKB];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const bf16x8 ka = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
+          const bf16x8 va = *(const bf16x8*)(vt + kb * 32 * D + koff[ks]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16{} : dp[kb], 0, 0, 0);
+        }
+      }
+      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff off - 4*lh <= lim
+      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
+      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
+      bf16x8 dsf[NKK];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 w;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int r = half * 8 + 2 * t;
+            float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+            float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -lse2));
+            if (masked) {
+              if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p0 = 0.f;
+              if (kb * 32 + 8 * ((r + 1) >> 2) + ((r + 1) & 3) > lim) p1 = 0.f;
+            }
+            w[t] = pack_bf16x2(p0 * (dp[kb][r] - dd), p1 * (dp[kb][r + 1] - dd));
+          }
+          dsf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 a = tr_operand(kt + kk * 16 * D, tro.lo[db], tro.hi[db]);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], acc[db], 0, 0, 0);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (myq < N) store_rows<NDB>((__bf16*)p.dq + head_base + (long long)myq * tok, acc, p.scale, lh);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV: per (batch, head, 256 key rows); 64-query Q / dO tiles.  Each of
+// the 8 waves (two per SIMD) owns 32 keys.  At D = 64 one kernel produces
+// both gradients (WANT = 3).  At D = 128 the K and V rows of a wave and two
+// 32 x 128 fp32 accumulators do not fit the 256 registers of a wave that
+// shares its SIMD, so two kernels run instead: dV (WANT = 1: S, P, dV^T) and
+// dK (WANT = 2: S, P, dP, dS, dK^T), which recompute S.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, int WANT>
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(WANT >= 1 && WANT <= 3, "dV (1), dK (2) or both (3)");
+  constexpr bool DV = (WANT & 1) != 0;
+  constexpr bool DK = (WANT & 2) != 0;
+  constexpr int NW = 8;
+  constexpr int BK = NW * 32, BQ = 64;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int TILE = BQ * D;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];
+  __shared__ __attribute__((aligned(16))) float rowv[2][2][BQ];   // [buffer][lse2, D][query]
+  __bf16* qs_base = smem;
+  __bf16* gs_base = smem + 2 * TILE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+
+  const int bh = blockIdx.x / p.n_ktiles;
+  const int kt = blockIdx.x - bh * p.n_ktiles;   // causal: low key tiles see the most queries
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int N = p.N;
+  const long long tok = (long long)p.H * D;
+  const long long head_base = ((long long)b * N * p.H + h) * D;
+  const int k0 = kt * BK;
+  const int kw0 = k0 + wave * 32;
+  const int mykey = kw0 + ln;
+  const int kr = mykey < N ? mykey : N - 1;
+
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
+  const __bf16* __restrict__ gg = (const __bf16*)p.dout + head_base;
+
+  // K^T and V^T fragments (B operands of S = Q K^T and dP = dO V^T): lane
+  // (n = ln, h = lh) holds row mykey, columns 16 ks + 8 lh .. +7
+  bf16x8 kf[NKS], vf[DK ? NKS : 1];
+  {
+    const u32x4* ks = (const u32x4*)(kg + (long long)kr * tok + 8 * lh);
+    const u32x4* vs = (const u32x4*)(vg + (long long)kr * tok + 8 * lh);
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      kf[i] = __builtin_bit_cast(bf16x8, ks[2 * i]);
+      if constexpr (DK) vf[i] = __builtin_bit_cast(bf16x8, vs[2 * i]);
+    }
+  }
+  const float c = p.c;
+
+  const int n_q_all = (N + BQ - 1) / BQ;
+  const int first = CAUSAL ? k0 / BQ : 0;
+
+  TileLoader<D, NW> ld;
+  ld.init(wave, lane, tok);
+  const unsigned lds_q = (unsigned)(size_t)((ATTN_LDS __bf16*)qs_base);
+  const unsigned lds_g = (unsigned)(size_t)((ATTN_LDS __bf16*)gs_base);
+  const float* __restrict__ lse_h = p.lse + (long long)bh * N;
+  const float* __restrict__ del_h = p.delta + (long long)bh * N;
+  // lse (log2 units) and D of the tile's 64 query rows, by wave 0
+  auto load_rows = [&](int qt0, int buf) {
+    if (wave == 0) {
+      const int r = min(qt0 + lane, N - 1);
+      rowv[buf][0][lane] = lse_h[r] * kLog2e;
+      rowv[buf][1][lane] = del_h[r];
+    }
+  };
+
+  int qoff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qoff[ks] = ln * D + (((2 * ks + lh) ^ swz_b<D>(ln)) * 8);
+  TrOffsets<D, NDB> tro;
+  tro.init(lane);
+
+  f32x16 dk[DK ? NDB : 1], dv[DV ? NDB : 1];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    if constexpr (DK) dk[db] = f32x16{};
+    if constexpr (DV) dv[db] = f32x16{};
+  }
+
+  if (first < n_q_all) {
+    ld.load(qg, tok, lds_q, first * BQ, N);
+    ld.load(gg, tok, lds_g, first * BQ, N);
+    load_rows(first * BQ, 0);
+  }
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = first; j < n_q_all; ++j) {
+    const int buf = (j - first) & 1;
+    if (j + 1 < n_q_all) {
+      const unsigned nb = (unsigned)((buf ^ 1) * TILE * 2);
+      ld.load(qg, tok, lds_q + nb, (j + 1) * BQ, N);
+      ld.load(gg, tok, lds_g + nb, (j + 1) * BQ, N);
+      load_rows((j + 1) * BQ, buf ^ 1);
+    }
+    const int qt0 = j * BQ;
+    // the wave's keys see this tile unless all its queries precede them
+    const bool active = kw0 < N && (!CAUSAL || qt0 + BQ - 1 >= kw0);
+    if (active) {
+      const __bf16* qt = qs_base + buf * TILE;
+      const __bf16* gt = gs_base + buf * TILE;
+      const bool masked = (qt0 + BQ > N) || (CAUSAL && qt0 < kw0 + 31);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 qa = *(const bf16x8*)(qt + qb * 32 * D + qoff[ks]);
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+          if constexpr (DK) {
+            const bf16x8 ga = *(const bf16x8*)(gt + qb * 32 * D + qoff[ks]);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+          }
+        }
+        // register r holds query qt0 + 32 qb + 8 (r/4) + 4 lh + r%4 of key mykey
+        bf16x8 pf[2], dsf[2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          u32x4 wp, wd;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int rb = 8 * g + 4 * half;                        // registers rb .. rb+3
+            const int qi = 32 * qb + 8 * (rb >> 2) + 4 * lh;        // their first tile row
+            const f32x4 lv = *(const f32x4*)&rowv[buf][0][qi];
+            const f32x4 dv4 = *(const f32x4*)&rowv[buf][1][qi];
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              float pe = fast_exp2(__builtin_fmaf(s[rb + x], c, -lv[x]));
+              if (masked) {
+                const int q = qt0 + qi + x;
+                if (q >= N || (CAUSAL && mykey > q)) pe = 0.f;
+              }
+              pv[x] = pe;
+              dsv[x] = pe * (dp[rb + x] - dv4[x]);
+            }
+            wp[2 * half] = pack_bf16x2(pv[0], pv[1]);
+            wp[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
+            wd[2 * half] = pack_bf16x2(dsv[0], dsv[1]);
+            wd[2 * half + 1] = pack_bf16x2(dsv[2], dsv[3]);
+          }
+          pf[g] = __builtin_bit_cast(bf16x8, wp);
+          dsf[g] = __builtin_bit_cast(bf16x8, wd);
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const int rowb = (32 * qb + 16 * g) * D;
+            if constexpr (DV) {
+              const bf16x8 ga = tr_operand(gt + rowb, tro.lo[db], tro.hi[db]);
+              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pf[g], dv[db], 0, 0, 0);
+            }
+            if constexpr (DK) {
+              const bf16x8 qa = tr_operand(qt + rowb, tro.lo[db], tro.hi[db]);
+              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[g], dk[db], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (mykey < N) {
+    if constexpr (DK) store_rows<NDB>((__bf16*)p.dk + head_base + (long long)mykey * tok, dk, p.scale, lh);
+    if constexpr (DV) store_rows<NDB>((__bf16*)p.dv + head_base + (long long)mykey * tok, dv, 1.f, lh);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch (called by the C ABI in attn_api.cpp)
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+static hipError_t launch_bwd_t(BwdParams prm, hipStream_t stream) {
+  const long long rows = (long long)prm.B * prm.N * prm.H;
+  const int grid_delta = (int)((rows + 15) / 16);
+  hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3(grid_delta), dim3(256), 0, stream, prm);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = prm.B * prm.H * prm.n_tiles;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(grid), dim3(512), 0, stream, prm);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  prm.n_ktiles = prm.n_tiles;
+  if constexpr (D == 128) {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, 1>), dim3(grid), dim3(512), 0, stream, prm);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, 2>), dim3(grid), dim3(512), 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, 3>), dim3(grid), dim3(512), 0, stream, prm);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           float* delta, int B, int H, int N, int d, int causal, float scale,
+                           hipStream_t stream) {
+  BwdParams prm = {};
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.o = o;
+  prm.lse = lse;
+  prm.dout = dout;
+  prm.dq = dq;
+  prm.dk = dk;
+  prm.dv = dv;
+  prm.delta = delta;
+  prm.B = B;
+  prm.H = H;
+  prm.N = N;
+  prm.n_tiles = (N + 255) / 256;
+  prm.scale = scale;
+  prm.c = scale * kLog2e;
+  if (d == 128) return causal ? launch_bwd_t<128, true>(prm, stream) : launch_bwd_t<128, false>(prm, stream);
+  return causal ? launch_bwd_t<64, true>(prm, stream) : launch_bwd_t<64, false>(prm, stream);
+}
+
+}  // namespace attn

@@ -161,6 +161,33 @@ int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, fl
                         const int* cu_seqlens, int B, int total, int max_seqlen, int H, int H_kv,
                         int d, int causal, float scale, hipStream_t stream);
 
+/*
+ * attn_bwd -- bfloat16 backward pass: the gradients of attn_fwd's output O
+ * with respect to q, k and v, given the upstream gradient dO.  The backward
+ * pass is named as the forward kernel's counterpart (needed for training) by
+ * "FlashAttention 4: Atenção Mais Rápida e Eficiente em Memória para LLMs",
+ * section "Principais Conclusões", and "FlashAttention-4 no Blackwell B200
+ * ...", section "Redução de tráfego no backward".  With P = softmax(scale
+ * Q K^T) (masked as in the forward):
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P * (dP - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ * P is recomputed tile by tile from lse; no N x N matrix reaches HBM.
+ *   q, k, v, o, dout : bf16 [B][N][H][d], device, read only; o and lse are
+ *                      the outputs of attn_fwd for the same q, k, v, causal
+ *                      and scale.
+ *   lse              : fp32 [B][H][N], device, read only.
+ *   dq, dk, dv       : bf16 [B][N][H][d], device, written.
+ *   delta            : fp32 [B][H][N], device, caller-owned workspace (the
+ *                      library allocates nothing); written with D.
+ *   B, H, N, d, causal, scale, stream : as for attn_fwd.
+ * Three kernels are enqueued on `stream` (D, then dQ, then dK/dV); the
+ * results are deterministic (no atomics).  Errors as for attn_fwd; null
+ * dout/dq/dk/dv/delta is ATTN_ERR_INVALID_ARG.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* delta,
+             int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);
 

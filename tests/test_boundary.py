@@ -32,8 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_fp8", "attn_fwd_gqa", "attn_fwd_varlen",
-                          "attn_fwd_fp8_gqa", "attn_fwd_fp8_varlen", "attn_status_string",
-                          "attn_version"}
+                          "attn_fwd_fp8_gqa", "attn_fwd_fp8_varlen", "attn_bwd",
+                          "attn_status_string", "attn_version"}
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -106,7 +106,15 @@ def call8_var(**kw):
                                    a["d"], a["causal"], a["scale"], None, check=False)
 
 
-ALL_CALLS = [call, call8, call_gqa, call8_gqa, call_var, call8_var]
+def call_bwd(**kw):
+    a = dict(GOOD, do=P + 0x7000, dq=P + 0x8000, dk=P + 0x9000, dv=P + 0xA000, delta=P + 0xB000)
+    a.update(kw)
+    return eat.attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                        a["dv"], a["delta"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                        a["scale"], None, check=False)
+
+
+ALL_CALLS = [call, call8, call_gqa, call8_gqa, call_var, call8_var, call_bwd]
 
 
 @pytest.mark.parametrize("fn", ALL_CALLS)
@@ -135,7 +143,7 @@ def test_invalid_arguments_rejected_on_host(lib, fn, kw, status):
     assert fn(**kw) == status
 
 
-@pytest.mark.parametrize("fn", [call, call8])
+@pytest.mark.parametrize("fn", [call, call8, call_bwd])
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
     (dict(B=1 << 30, N=1 << 30, H=1 << 30), eat.ATTN_ERR_INVALID_ARG),
@@ -182,3 +190,16 @@ def test_fp8_requires_descales(lib, fn, kw):
 def test_binding_raises_with_status_name(lib):
     with pytest.raises(eat.AttnError, match="ATTN_ERR_UNSUPPORTED"):
         eat.attn_fwd(P, P, P, P, P, 1, 1, 16, 80, 0, 1.0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(do=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(dq=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(dk=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(dv=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(delta=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(dq=P + 0x8008), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(delta=P + 0xB002), eat.ATTN_ERR_UNSUPPORTED),
+])
+def test_backward_buffers_checked(lib, kw, status):
+    assert call_bwd(**kw) == status

@@ -223,6 +223,13 @@ def make_fp8(w, shape=None):
     return out
 
 
+def make_dout(w, shape=None):
+    """Upstream gradient dO for a backward pass: bf16 bits of N(0,1),
+    shaped like Q ([B][N][H][d]), seed tensor id 9."""
+    (B, N, H, d), shp = _shapes(w, shape)
+    return bf16_bits(_randn(shp["q"], seed_for(w.wid, 9)))
+
+
 def make_inputs(w, shape=None):
     return make_fp8(w, shape) if w.dtype == "fp8" else make_bf16(w, shape)
 
