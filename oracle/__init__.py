@@ -23,6 +23,8 @@ grouped     grouped-query (K/V heads shared by groups of query heads) and
             variable-length (packed sequences) forms of the definition.
 backward    the gradients dQ, dK, dV of the definition (chain rule), and the
             row quantity D = sum(dO * O).
+quantize    E4M3 encoding and per-(batch, head) quantisation of attention
+            inputs with the optional random Hadamard rotation.
 """
 
 from .formats import bf16_bits_to_float64, e4m3fn_bits_to_float64, dequantize_e4m3
@@ -31,6 +33,7 @@ from .tiled import tiled_online_softmax_head, simulator_counts
 from .brute import attention_brute
 from .grouped import attention_forward_gqa, attention_forward_varlen
 from .backward import attention_backward, attention_backward_head, attention_delta
+from .quantize import e4m3fn_encode, fwht32, hadamard, quantize_e4m3
 
 __all__ = [
     "bf16_bits_to_float64",
@@ -46,4 +49,8 @@ __all__ = [
     "attention_backward",
     "attention_backward_head",
     "attention_delta",
+    "e4m3fn_encode",
+    "fwht32",
+    "hadamard",
+    "quantize_e4m3",
 ]
