@@ -33,6 +33,11 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # 256 CU x 2.4 GHz dense MFMA
 METRIC = "attn fwd TFLOPS (4BHN²d, causal halved) + % of MI355X MFMA peak, 1 GPU"
 METRIC_BWD = "attn bwd TFLOPS (2.5 x 4BHN²d, causal halved) + % of MI355X MFMA peak, 1 GPU"
+METRIC_QUANT = ("fp8 input quantisation GB/s (Q, K rotated + V; 3 B per element: bf16 in, "
+                "e4m3 out) + % of MI355X HBM peak, 1 GPU")
+PEAK_HBM_GBS = 8000.0
+METRIC_FWD2 = ("attn fwd fp8 two-pass TFLOPS (4BHN²d, causal halved; the row-maximum pass is "
+               "not counted) + % of MI355X MFMA peak, 1 GPU")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
@@ -153,6 +158,50 @@ def cpu_baseline(w, inp, causal, budget_s=12.0):
     }
 
 
+def quant_line(args, w, ms_per_step, avg_launch_ms, src_elems):
+    """The JSON line of --pass quant: bytes are algorithmic (each bf16 input
+    element read once, each code written once); the second read pass of the
+    two-pass quantiser is overhead, visible in the measured traffic."""
+    nbytes = 3.0 * src_elems
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_launch_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC_QUANT, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded, workloads/)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "pass": "quant",
+                   "rotation": "Q and K (random Hadamard), V plain"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel_avg_ms": round(avg_launch_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = quant_cpu_baseline(w)
+    return out
+
+
+def quant_cpu_baseline(w):
+    """The oracle's quantiser (rotation on) on one (batch, head) of Q at the
+    full sequence length, scaled to GB/s of the same algorithmic bytes."""
+    from oracle import bf16_bits_to_float64, quantize_e4m3
+    from workloads import make_bf16, rotation_signs
+    x = bf16_bits_to_float64(make_bf16(w)["q"][:1, :, :1, :])
+    signs, _ = rotation_signs(w)
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        quantize_e4m3(x, signs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or reps >= 50:
+            break
+    gbs = 3.0 * x.size * reps / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "one (batch, head) of Q, %d rows x d=%d, rotation on, %d repetitions"
+                      % (w.N, w.d, reps)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,8 +210,10 @@ def main():
     ap.add_argument("--workload", default="long8k")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd",
-                    help="time the forward (default) or the backward pass (bf16 workloads)")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "fwd2", "bwd", "quant"], default="fwd",
+                    help="time the forward (default), the two-pass fp8 forward (fwd2), the "
+                         "backward pass (bf16 workloads) or the E4M3 quantisation of the "
+                         "inputs (fp8 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 1 GiB device copy (for counter scaling)")
     args = ap.parse_args()
@@ -199,7 +250,15 @@ def main():
         dk = torch.from_numpy(inp["dk"]).reshape(-1).to(dev)
         dv = torch.from_numpy(inp["dv"]).reshape(-1).to(dev)
 
-        if w.varlen:
+        if args.which == "fwd2":
+            if w.varlen:
+                print("--pass fwd2 takes a fixed-length fp8 workload", file=sys.stderr)
+                sys.exit(2)
+
+            def step():
+                eat.attn_fwd_fp8_2pass(q, k, v, o, lse, dq, dk, dv, w.B, w.H, Hkv, w.N, w.d,
+                                       int(causal), w.scale, stream)
+        elif w.varlen:
             def step():
                 eat.attn_fwd_fp8_varlen(q, k, v, o, lse, dq, dk, dv, cu, w.B, T, w.N, w.H, Hkv,
                                         w.d, int(causal), w.scale, stream)
@@ -208,6 +267,10 @@ def main():
                 eat.attn_fwd_fp8_gqa(q, k, v, o, lse, dq, dk, dv, w.B, w.H, Hkv, w.N, w.d,
                                      int(causal), w.scale, stream)
     else:
+        if args.which == "fwd2":
+            print("--pass fwd2 takes an fp8 workload", file=sys.stderr)
+            sys.exit(2)
+
         def dev16(x):
             return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         q, k, v = dev16(inp["q"]), dev16(inp["k"]), dev16(inp["v"])
@@ -241,6 +304,25 @@ def main():
             eat.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, w.B, w.H, w.N, w.d, int(causal),
                          w.scale, stream)
 
+    if args.which == "quant":
+        if w.dtype != "fp8" or w.varlen:
+            print("--pass quant takes a fixed-length fp8 workload", file=sys.stderr)
+            sys.exit(2)
+        from workloads import make_bf16, rotation_signs
+        src = make_bf16(w)
+        qb, kb, vb = (torch.from_numpy(src[n].view(np.int16)).to(dev).view(torch.bfloat16)
+                      for n in "qkv")
+        del src
+        _, words = rotation_signs(w)
+        sw = torch.from_numpy(words.view(np.int32)).to(dev)
+        for t in (q, k, v, dq, dk, dv):
+            t.zero_()
+
+        def step():
+            eat.attn_fp8_quantize(qb, q, dq, sw, w.B, w.N, w.H, w.d, stream)
+            eat.attn_fp8_quantize(kb, k, dk, sw, w.B, w.N, Hkv, w.d, stream)
+            eat.attn_fp8_quantize(vb, v, dv, None, w.B, w.N, Hkv, w.d, stream)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -272,9 +354,19 @@ def main():
         del src, dst
 
     outs = [lse, o] + ([dq, dk, dv] if args.which == "bwd" else [])
+    if args.which == "quant":
+        outs = [dq, dk, dv]
+        if not all(bool((x > 0).all()) for x in outs):
+            print("quantiser wrote no descale", file=sys.stderr)
+            sys.exit(1)
     if not all(bool(torch.isfinite(x.float()).all()) for x in outs):
         print("non-finite output", file=sys.stderr)
         sys.exit(1)
+
+    if args.which == "quant":
+        print(json.dumps(quant_line(args, w, ms_per_step, avg_launch_ms, src_elems=(
+            w.B * w.N * (w.H + 2 * Hkv) * w.d))), flush=True)
+        return
 
     flops = w.flops(causal) * (2.5 if args.which == "bwd" else 1.0)
     peak = PEAK_TFLOPS[w.dtype]
@@ -303,10 +395,12 @@ def main():
                      "traffic": measured_traffic(w.name, w.dtype, causal),
                      "kernel_avg_ms": round(avg_launch_ms, 4)},
     }
-    if args.which == "bwd":
-        out["config"]["pass"] = "bwd"
+    if args.which in ("bwd", "fwd2"):
+        out["config"]["pass"] = args.which
         out["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline and args.which == "fwd":
+    if args.which == "fwd2":
+        out["metric"] = METRIC_FWD2
+    if not args.no_cpu_baseline and args.which in ("fwd", "fwd2"):
         out["cpu_baseline"] = cpu_baseline(w, inp, causal)
     print(json.dumps(out), flush=True)
 

@@ -60,6 +60,10 @@ def load_library():
     lib.attn_fwd_fp8_varlen.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_bwd.restype = i
+    lib.attn_fwd_fp8_2pass.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_fp8_2pass.restype = i
+    lib.attn_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+    lib.attn_fp8_quantize.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -171,4 +175,28 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale
                                  int(N), int(d), int(causal), float(scale), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
+    return st
+
+
+def attn_fp8_quantize(x, codes, descale, sign_bits, B, N, H, d, stream=None, check=True):
+    """bf16 -> E4M3 codes + per-(batch, head) descale, optionally rotated;
+    see attn_fp8_quantize in include/attn.h (``sign_bits`` None: no
+    rotation)."""
+    st = load_library().attn_fp8_quantize(_ptr(x), _ptr(codes), _ptr(descale), _ptr(sign_bits),
+                                          int(B), int(N), int(H), int(d), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_quantize")
+    return st
+
+
+def attn_fwd_fp8_2pass(q, k, v, o, lse, descale_q, descale_k, descale_v, B, H, H_kv, N, d, causal,
+                       scale, stream=None, check=True):
+    """Two-pass OCP e4m3 forward (exact row maximum first); see
+    attn_fwd_fp8_2pass in include/attn.h."""
+    st = load_library().attn_fwd_fp8_2pass(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                           _ptr(descale_q), _ptr(descale_k), _ptr(descale_v),
+                                           int(B), int(H), int(H_kv), int(N), int(d),
+                                           int(causal), float(scale), _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_fp8_2pass")
     return st

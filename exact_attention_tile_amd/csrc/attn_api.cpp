@@ -15,11 +15,14 @@ namespace attn {
 int bf16_rows_per_block(int d);
 hipError_t launch_bf16(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream);
 int fp8_rows_per_block(int d);
-hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream);
+hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, bool two_pass,
+                      hipStream_t stream);
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* delta, int B, int H, int N, int d, int causal, float scale,
                            hipStream_t stream);
+hipError_t launch_quant(const void* x, void* codes, float* descale, const unsigned* signs, int B,
+                        int N, int H, int d, hipStream_t stream);
 }  // namespace attn
 
 namespace {
@@ -106,12 +109,14 @@ int run_bf16(attn::FwdParams& prm, int d, int causal, float scale, hipStream_t s
   return attn::launch_bf16(prm, d, causal, grid, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
-int run_fp8(attn::FwdParams& prm, int d, int causal, float scale, hipStream_t stream) {
+int run_fp8(attn::FwdParams& prm, int d, int causal, float scale, hipStream_t stream,
+            bool two_pass = false) {
   set_scale(prm, scale, 0x80808080u);
   int grid = 0;
   const int st = plan(prm, attn::fp8_rows_per_block(d), &grid);
   if (st != ATTN_OK) return st;
-  return attn::launch_fp8(prm, d, causal, grid, stream) == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return attn::launch_fp8(prm, d, causal, grid, two_pass, stream) == hipSuccess ? ATTN_OK
+                                                                                : ATTN_ERR_HIP;
 }
 
 // Fixed-length call with Hkv K/V heads.
@@ -239,6 +244,38 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   if (grid > INT32_MAX || (tokens * H + 15) / 16 > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
   const hipError_t e = attn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N,
                                              d, causal, scale, stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_fwd_fp8_2pass(const void* q, const void* k, const void* v, void* o,
+                                  float* lse, const float* descale_q, const float* descale_k,
+                                  const float* descale_v, int B, int H, int H_kv, int N, int d,
+                                  int causal, float scale, hipStream_t stream) {
+  attn::FwdParams prm = {};
+  int st = fixed_params(prm, q, k, v, o, lse, B, H, H_kv, N, d, causal, scale);
+  if (st != ATTN_OK) return st;
+  st = validate_descales(descale_q, descale_k, descale_v);
+  if (st != ATTN_OK) return st;
+  prm.dq = descale_q;
+  prm.dk = descale_k;
+  prm.dv = descale_v;
+  return run_fp8(prm, d, causal, scale, stream, true);
+}
+
+extern "C" int attn_fp8_quantize(const void* x, void* codes, float* descale,
+                                 const unsigned* sign_bits, int B, int N, int H, int d,
+                                 hipStream_t stream) {
+  if (!x || !codes || !descale) return ATTN_ERR_INVALID_ARG;
+  int64_t tokens = 0;
+  int st = validate_fixed(B, N, &tokens);
+  if (st != ATTN_OK) return st;
+  if (H <= 0) return ATTN_ERR_INVALID_ARG;
+  if (tokens > (INT64_MAX / 4) / H || tokens * H > (INT64_MAX / 4) / 128) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(codes)) return ATTN_ERR_UNSUPPORTED;
+  if (((uintptr_t)descale & 3u) || ((uintptr_t)sign_bits & 3u)) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * ((N + 127) / 128) > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+  const hipError_t e = attn::launch_quant(x, codes, descale, sign_bits, B, N, H, d, stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

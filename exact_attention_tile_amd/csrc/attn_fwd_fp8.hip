@@ -31,6 +31,16 @@
 // 2^(TAU + P_OFFSET) = 256 < 448, rounded to e4m3 (RNE, v_cvt_pk_fp8_f32);
 // the row sum l is accumulated from the fp32 p'; O = acc * dv / l, so the
 // 2^P_OFFSET factor cancels; lse = ln2 * (m_ref - P_OFFSET + log2 l).
+//
+// Two-pass form (same section of the FA3 page: a first pass finds each row's
+// exact maximum of the scores with fp32 accumulation, the second
+// exponentiates and multiplies by V with static scale factors).  MODE 1
+// runs only S^T = K Q^T and the row maximum m = max_j s_ij c over the
+// visible keys, and stores m where lse goes; MODE 2 reads it back and runs
+// the product with m fixed: no running maximum and no rescale, and
+// p' = exp2(s c - m + 8) <= 2^8 for every key (the static scale 2^8 keeps
+// p' inside e4m3's normal range down to p = 2^-14).  MODE 0 is the
+// single-pass kernel.
 #include <type_traits>
 
 #include "attn_kernels.hpp"
@@ -39,6 +49,7 @@ namespace attn {
 
 constexpr float kTauFp8 = 4.0f;
 constexpr float kPOffset = 4.0f;   // kTauFp8 + kPOffset <= 8 keeps p' <= 256
+constexpr float kPOffset2 = 8.0f;  // two-pass: the exact maximum gives p' <= 2^8
 
 // 16-byte-chunk XOR swizzles of the row-major [BC][D]-byte LDS tiles (rows
 // of D bytes; a 256-byte bank line spans 256/D rows).
@@ -62,8 +73,9 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-template <int D, int NW, int BC, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
+  static_assert(MODE >= 0 && MODE <= 2, "0 single pass, 1 row maximum, 2 fixed maximum");
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BC == 64 || BC == 128, "kv tile");
   static_assert(NW == 8, "two groups of four waves, one wave of each per SIMD");
@@ -213,6 +225,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   float m_ref = -__builtin_inff();
+  if constexpr (MODE == 2) m_ref = p.lse[sv.lse_base + (myq < N ? myq : N - 1)];
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
   f32x16 s[NKB];
   i32x8 pf[NKK];
@@ -292,6 +305,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
     }
+    if constexpr (MODE != 2) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -299,6 +313,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
     mx = pair_max(mx);
     const float mt = mx * c;
+    if constexpr (MODE == 1) {
+      m_ref = fmaxf(m_ref, mt);
+      return;
+    }
     const bool need = mt > m_ref + kTauFp8;
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
@@ -310,11 +328,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
+    }
     // p' = exp2(s c - m_ref + P_OFFSET), in place: all FMAs, all
     // exponentials, then the e4m3 packs (64-key step kk, slot t = 16 (kb & 1)
     // + r) and the row sums (four chains), so that no instruction waits on
     // the one just before it
-    const float bias = kPOffset - m_ref;
+    const float bias = (MODE == 2 ? kPOffset2 : kPOffset) - m_ref;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -366,14 +385,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     if (grp == 0 && (ph & 1) == 0) {
       const int u = ph >> 1;
       if (u + 1 < wg_tiles) load_k(u + 1);
-      if (u < wg_tiles) load_v(u);
+      if (MODE != 1 && u < wg_tiles) load_v(u);
     }
     const int q = ph - grp;
     if (q >= 0) {
       if ((q & 1) == 0) {
         const int j = (q >> 1) - 1;
         const bool qk = j + 1 < wv_tiles;
-        const bool pv = j >= 0 && j < wv_tiles;
+        const bool pv = MODE != 1 && j >= 0 && j < wv_tiles;
         const unsigned char* kt = ks_base + ((j + 1) & 1) * TILE;
         const unsigned char* vt = vs_base + (j & 1) * TILE;
         if (qk && pv)
@@ -398,6 +417,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     __syncthreads();
   }
 
+  if constexpr (MODE == 1) {
+    if (myq < N && lh == 0) p.lse[sv.lse_base + myq] = m_ref;
+    return;
+  }
   // ---- epilogue: O = acc dv / l -> bf16, lse = ln2 (m_ref - offset + log2 l)
   const float l_tot = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
   if (myq < N) {
@@ -416,15 +439,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     }
     if (lh == 0) {
       p.lse[sv.lse_base + myq] =
-          (m_ref - kPOffset + fast_log2(l_tot)) * 0.69314718055994531f;
+          (m_ref - (MODE == 2 ? kPOffset2 : kPOffset) + fast_log2(l_tot)) * 0.69314718055994531f;
     }
   }
 }
 
 template <int D, int NW, int BC, bool CAUSAL>
-static hipError_t launch_fp8_t(const FwdParams& prm, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream,
-                     prm);
+static hipError_t launch_fp8_t(const FwdParams& prm, int grid, bool two_pass, hipStream_t stream) {
+  if (!two_pass) {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 0>), dim3(grid), dim3(NW * 64), 0,
+                       stream, prm);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 1>), dim3(grid), dim3(NW * 64), 0,
+                       stream, prm);
+    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 2>), dim3(grid), dim3(NW * 64), 0,
+                       stream, prm);
+  }
   return hipGetLastError();
 }
 
@@ -436,13 +466,14 @@ constexpr int kFp8Tile = 128;
 
 int fp8_rows_per_block(int d) { return kFp8Waves * 32; }
 
-hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream) {
+hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, bool two_pass,
+                      hipStream_t stream) {
   if (d == 128) {
-    return causal ? launch_fp8_t<128, kFp8Waves, kFp8Tile, true>(prm, grid, stream)
-                  : launch_fp8_t<128, kFp8Waves, kFp8Tile, false>(prm, grid, stream);
+    return causal ? launch_fp8_t<128, kFp8Waves, kFp8Tile, true>(prm, grid, two_pass, stream)
+                  : launch_fp8_t<128, kFp8Waves, kFp8Tile, false>(prm, grid, two_pass, stream);
   }
-  return causal ? launch_fp8_t<64, kFp8Waves, kFp8Tile, true>(prm, grid, stream)
-                : launch_fp8_t<64, kFp8Waves, kFp8Tile, false>(prm, grid, stream);
+  return causal ? launch_fp8_t<64, kFp8Waves, kFp8Tile, true>(prm, grid, two_pass, stream)
+                : launch_fp8_t<64, kFp8Waves, kFp8Tile, false>(prm, grid, two_pass, stream);
 }
 
 }  // namespace attn

@@ -152,6 +152,24 @@ int attn_fwd_fp8_gqa(const void* q, const void* k, const void* v, void* o, float
                      hipStream_t stream);
 
 /*
+ * attn_fwd_fp8_2pass -- attn_fwd_fp8_gqa in the two-pass form of
+ * "FlashAttention-3: Pipeline Assíncrono com Warp Specialization, WGMMA e
+ * FP8 no Hopper e Blackwell", section "Estabilidade em FP8: Algoritmo de 2
+ * Passos e Incoherent Processing": a first pass computes every row's exact
+ * maximum score (fp32 accumulation of the e4m3 products) and stores it in
+ * lse; a second pass exponentiates against that fixed maximum and
+ * multiplies by V with a static scale on P (p' = 2^8 p, rounded to e4m3),
+ * with no running maximum and no rescale.  Same arguments, layouts,
+ * results (o, lse) and errors as attn_fwd_fp8_gqa; lse also carries the
+ * row maxima between the two kernels, which are enqueued on `stream` in
+ * order.  It costs about one and a half times the single pass.
+ */
+int attn_fwd_fp8_2pass(const void* q, const void* k, const void* v, void* o, float* lse,
+                       const float* descale_q, const float* descale_k, const float* descale_v,
+                       int B, int H, int H_kv, int N, int d, int causal, float scale,
+                       hipStream_t stream);
+
+/*
  * attn_fwd_fp8_varlen -- OCP FP8 E4M3 form of attn_fwd_varlen.
  *   q : e4m3fn [total][H][d];  k, v : e4m3fn [total][H_kv][d];  o : bf16 [total][H][d];
  *   lse : fp32 [H][total];  descales per (sequence b, head) as for attn_fwd_fp8_gqa.
@@ -180,13 +198,47 @@ int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, fl
  *   delta            : fp32 [B][H][N], device, caller-owned workspace (the
  *                      library allocates nothing); written with D.
  *   B, H, N, d, causal, scale, stream : as for attn_fwd.
- * Three kernels are enqueued on `stream` (D, then dQ, then dK/dV); the
- * results are deterministic (no atomics).  Errors as for attn_fwd; null
+ * The kernels are enqueued on `stream` in order: D, dQ, then dK/dV (at
+ * d = 128 dV and dK are separate launches); the results are deterministic
+ * (no atomics).  Errors as for attn_fwd; null
  * dout/dq/dk/dv/delta is ATTN_ERR_INVALID_ARG.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, float* delta,
              int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
+/*
+ * attn_fp8_quantize -- bfloat16 attention input -> OCP FP8 E4M3 codes and a
+ * per-(batch, head) descale, the input format of the FP8 entry points, with
+ * the optional random Hadamard rotation of "FlashAttention-3: Pipeline
+ * Assíncrono com Warp Specialization, WGMMA e FP8 no Hopper e Blackwell",
+ * section "Estabilidade em FP8: Algoritmo de 2 Passos e Incoherent
+ * Processing" (incoherent processing: a random orthogonal Hadamard matrix
+ * spreads outliers over all dimensions).  With M = diag(s) H_d / sqrt(d)
+ * (s the random signs, H_d the Sylvester Hadamard matrix), rotating Q and K
+ * with the same signs leaves Q K^T unchanged; V is quantised unrotated.
+ *   x         : bf16 [B][N][H][d], device, read only, finite values.
+ *   codes     : e4m3fn [B][N][H][d], device, written (its first
+ *               4 * B * H * ceil(N / 128) bytes hold per-work-group partial
+ *               maxima until the codes overwrite them).
+ *   descale   : fp32 [B][H], device, written (also used as the per-head
+ *               maximum while the call runs).
+ *   sign_bits : device, d/32 words, bit i of the words = sign of column i
+ *               (1: negate); NULL = no rotation.
+ * Per (b, h): y = x diag(s) H_d (binary32 fast Walsh-Hadamard butterfly,
+ * strides 1, 2, ..., d/2) or y = x; amax = max |y|; ds = amax / 448;
+ * code = e4m3(clamp(y / ds, +-448)) rounded to nearest even (ds = 0 divides
+ * by 1); descale = ds, or ds / sqrt(d) rounded to binary32 with the
+ * rotation, so that code * descale approximates x M.  Every decision is
+ * taken in binary32 and the codes are bit-reproducible.
+ * d is 64 or 128.  Four kernels are enqueued on `stream`; calls that share
+ * descale must not overlap.  Errors: null x/codes/descale, B, N or H <= 0:
+ * ATTN_ERR_INVALID_ARG; other d, x or codes not 16-byte aligned, descale or
+ * sign_bits not 4-byte aligned, more than 2^31 - 1 work-groups:
+ * ATTN_ERR_UNSUPPORTED; a launch failure: ATTN_ERR_HIP.
+ */
+int attn_fp8_quantize(const void* x, void* codes, float* descale, const unsigned* sign_bits,
+                      int B, int N, int H, int d, hipStream_t stream);
 
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);

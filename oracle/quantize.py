@@ -45,7 +45,7 @@ def e4m3fn_encode(x):
     definition (exponent bias 7, 3 mantissa bits, subnormals m/8 * 2^-6)."""
     x = np.asarray(x, dtype=np.float64)
     sign = np.signbit(x).astype(np.uint8) << np.uint8(7)
-    a = np.minimum(np.abs(x), E4M3_MAX)
+    a = np.minimum(np.abs(np.where(np.isnan(x), 0.0, x)), E4M3_MAX)
     code = np.zeros(a.shape, dtype=np.uint8)
     sub = a < 2.0 ** -6
     # subnormals (and the rounding up into the smallest normal): m = a / 2^-9

@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_fp8", "attn_fwd_gqa", "attn_fwd_varlen",
-                          "attn_fwd_fp8_gqa", "attn_fwd_fp8_varlen", "attn_bwd",
+                          "attn_fwd_fp8_gqa", "attn_fwd_fp8_varlen", "attn_bwd", "attn_fp8_quantize",
+                          "attn_fwd_fp8_2pass",
                           "attn_status_string", "attn_version"}
 
 
@@ -114,7 +115,15 @@ def call_bwd(**kw):
                         a["scale"], None, check=False)
 
 
-ALL_CALLS = [call, call8, call_gqa, call8_gqa, call_var, call8_var, call_bwd]
+def call8_2p(**kw):
+    a = dict(GOOD, Hkv=1, dq=P + 0x5000, dk=P + 0x5100, dv=P + 0x5200)
+    a.update(kw)
+    return eat.attn_fwd_fp8_2pass(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dq"], a["dk"],
+                                  a["dv"], a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                  a["scale"], None, check=False)
+
+
+ALL_CALLS = [call, call8, call_gqa, call8_gqa, call_var, call8_var, call_bwd, call8_2p]
 
 
 @pytest.mark.parametrize("fn", ALL_CALLS)
@@ -143,7 +152,7 @@ def test_invalid_arguments_rejected_on_host(lib, fn, kw, status):
     assert fn(**kw) == status
 
 
-@pytest.mark.parametrize("fn", [call, call8, call_bwd])
+@pytest.mark.parametrize("fn", [call, call8, call_bwd, call8_2p])
 @pytest.mark.parametrize("kw,status", [
     (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
     (dict(B=1 << 30, N=1 << 30, H=1 << 30), eat.ATTN_ERR_INVALID_ARG),
@@ -153,7 +162,7 @@ def test_fixed_length_sizes(lib, fn, kw, status):
     assert fn(**kw) == status
 
 
-@pytest.mark.parametrize("fn", [call_gqa, call8_gqa, call_var, call8_var])
+@pytest.mark.parametrize("fn", [call_gqa, call8_gqa, call_var, call8_var, call8_2p])
 @pytest.mark.parametrize("kw,status", [
     (dict(Hkv=0), eat.ATTN_ERR_INVALID_ARG),
     (dict(Hkv=-2), eat.ATTN_ERR_INVALID_ARG),
@@ -181,7 +190,7 @@ def test_varlen_sizes(lib, fn, kw, status):
     assert fn(**kw) == status
 
 
-@pytest.mark.parametrize("fn", [call8, call8_gqa, call8_var])
+@pytest.mark.parametrize("fn", [call8, call8_gqa, call8_var, call8_2p])
 @pytest.mark.parametrize("kw", [dict(dq=0), dict(dk=0), dict(dv=0)])
 def test_fp8_requires_descales(lib, fn, kw):
     assert fn(**kw) == eat.ATTN_ERR_INVALID_ARG
@@ -203,3 +212,31 @@ def test_binding_raises_with_status_name(lib):
 ])
 def test_backward_buffers_checked(lib, kw, status):
     assert call_bwd(**kw) == status
+
+
+def call_quant(**kw):
+    a = dict(x=P, codes=P + 0x1000, descale=P + 0x2000, signs=P + 0x3000, B=2, N=128, H=4, d=128)
+    a.update(kw)
+    return eat.attn_fp8_quantize(a["x"], a["codes"], a["descale"], a["signs"], a["B"], a["N"],
+                                 a["H"], a["d"], None, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(codes=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(descale=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(H=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(H=-3), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=1 << 30, N=1 << 30, H=1 << 30), eat.ATTN_ERR_INVALID_ARG),
+    (dict(d=96), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(d=32), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(x=P + 8), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(codes=P + 0x1004), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(descale=P + 0x2002), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(signs=P + 0x3001), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(B=65535, H=65535, N=1 << 20), eat.ATTN_ERR_UNSUPPORTED),   # grid beyond 2^31 blocks
+])
+def test_quantize_arguments_rejected_on_host(lib, kw, status):
+    assert call_quant(**kw) == status

@@ -91,3 +91,32 @@ def test_varlen_layout_and_offsets():
         if s1 > s0:
             for h in range(4):
                 assert (x["q"][0, s0:s1, h] & 0x7F).max() == 0x7E
+
+
+def test_rotation_signs_and_bits_agree():
+    from workloads import rotation_signs
+    w = WORKLOADS["fp8_8k"]
+    s, words = rotation_signs(w)
+    assert s.shape == (w.d,) and words.shape == (w.d // 32,) and words.dtype == np.uint32
+    bits = np.array([(int(words[i // 32]) >> (i % 32)) & 1 for i in range(w.d)])
+    assert np.array_equal(bits == 1, s < 0)
+    assert 0.3 < np.mean(s < 0) < 0.7
+    s2, words2 = rotation_signs(w)
+    assert np.array_equal(s, s2) and np.array_equal(words, words2)
+
+
+def test_bf16_source_of_outlier_workload_has_the_outliers():
+    # the bf16 input of an outlier workload carries the x20 outliers at the
+    # same positions as the fp8 workload's float32 draws
+    from workloads import make_bf16
+    w = Workload("o", 98, 1, 2, 500, 64, "fp8", (False,), outliers=True)
+    plain = Workload("p", 98, 1, 2, 500, 64, "bf16", (False,))
+    a = bf16_to_f32(make_bf16(w)["k"])
+    b = bf16_to_f32(make_bf16(plain)["k"])
+    changed = a != b
+    assert changed.sum() == round(0.001 * a.size)
+    assert np.allclose(a[changed], 20 * b[changed], rtol=1e-2)
+
+
+def bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)

@@ -25,13 +25,15 @@ along the token axis ([total][heads][d], offsets in "cu").
 Recipe (all draws on the CPU with torch.Generator, so the same seed gives the
 same bytes on every machine running this torch build):
   * seed = 1000 * workload_id + tensor_id, tensor ids Q=0, K=1, V=2,
-    peaked K rows=3, outlier positions=4 (+ the tensor id * 10), row sample=5;
+    peaked K rows=3, outlier positions=4 (+ the tensor id * 10), row sample=5,
+    sequence lengths=6, rotation signs=7, upstream gradient=9;
   * values: float32 standard normal, laid out [B][N][H][d];
   * ctx32k: per (b, h), round(0.01 * N) distinct key rows are multiplied by 8
     in float32 (a peaked softmax that exercises the rescale);
   * bf16: float32 -> bfloat16 round-to-nearest-even (torch's conversion);
-  * fp8: per tensor, round(0.001 * numel) distinct elements are multiplied by
-    20; then per (b, h): descale = amax / 448 and code = e4m3fn(x / descale)
+  * outliers (fp8_8k, and its bf16 source for the quantiser): per tensor,
+    round(0.001 * numel) distinct elements are multiplied by 20 in float32;
+  * fp8: the outliers as above; then per (b, h): descale = amax / 448 and code = e4m3fn(x / descale)
     round-to-nearest-even (torch's float8_e4m3fn conversion, after a clamp
     to +-448 so rounding noise cannot overflow);
   * sampled rows (large workloads): per (b, h), rows 0 and N-1 plus 510
@@ -177,10 +179,20 @@ def make_bf16(w, shape=None):
         x = _randn(shp[name], seed_for(w.wid, tid))
         if name == "k" and w.peaked_k:
             _peak_rows(w, x, N)
+        if w.outliers:
+            _outliers(w, x, tid)
         out[name] = bf16_bits(x)
     if w.lengths:
         out["cu"] = cu_seqlens(w.lengths)
     return out
+
+
+def _outliers(w, x, tid):
+    """Multiplies round(0.001 * numel) distinct elements of x by 20."""
+    n_out = int(round(0.001 * x.numel()))
+    idx = _perm_prefix(x.numel(), n_out, seed_for(w.wid, 4) + 10 * tid)
+    flat = x.view(-1)
+    flat[idx] *= 20.0
 
 
 def _quantize(x, descale_of):
@@ -197,10 +209,7 @@ def make_fp8(w, shape=None):
     for tid, name in enumerate(("q", "k", "v")):
         x = _randn(shp[name], seed_for(w.wid, tid))
         if w.outliers:
-            n_out = int(round(0.001 * x.numel()))
-            idx = _perm_prefix(x.numel(), n_out, seed_for(w.wid, 4) + 10 * tid)
-            flat = x.view(-1)
-            flat[idx] *= 20.0
+            _outliers(w, x, tid)
         if w.lengths:
             cu = cu_seqlens(w.lengths)
             nh = x.shape[2]
@@ -228,6 +237,19 @@ def make_dout(w, shape=None):
     shaped like Q ([B][N][H][d]), seed tensor id 9."""
     (B, N, H, d), shp = _shapes(w, shape)
     return bf16_bits(_randn(shp["q"], seed_for(w.wid, 9)))
+
+
+def rotation_signs(w):
+    """Random signs s for the Hadamard rotation diag(s) H_d / sqrt(d):
+    (float64 +-1 [d], uint32 [d/32] with bit i set where s_i = -1),
+    seed tensor id 7."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(w.wid, 7))
+    neg = (torch.randint(0, 2, (w.d,), generator=g) == 1).numpy()
+    words = np.zeros(w.d // 32, dtype=np.uint32)
+    for i in np.nonzero(neg)[0]:
+        words[i // 32] |= np.uint32(1) << np.uint32(i % 32)
+    return np.where(neg, -1.0, 1.0), words
 
 
 def make_inputs(w, shape=None):
