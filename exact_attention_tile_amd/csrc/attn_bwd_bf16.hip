@@ -55,12 +55,18 @@ struct BwdParams {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// 16-byte-chunk XOR swizzle of the row-major [rows][D] LDS tiles: a
-// ds_read_b128 of 16 lanes on 16 consecutive rows at one chunk hits
-// distinct banks.  The transposing reads of the same tiles see at most a
-// 2-way conflict.
+// 16-byte-chunk XOR swizzle of the row-major [rows][D] LDS tiles, read
+// two ways: a ds_read_b128 of 16 lanes takes one chunk of 16 consecutive
+// rows, so the swizzle must be a bijection over them (over the 8 rows of
+// one parity at D = 64, where a 256-byte bank line holds two rows); a
+// transposing read takes 4 consecutive chunks of 8 consecutive rows, so the
+// swizzle's high bits must put those rows' chunk groups on all four 64-byte
+// quarters of the bank line, twice each.  Both reads are then free of bank
+// conflicts.
 template <int D> __device__ __forceinline__ int swz_b(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  const int k = (row >> 1) & 7;
+  return k ^ ((k & 1) << 2);
 }
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) {
@@ -106,14 +112,14 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
   }
 }
 
-// Tile loader shared by the dQ and dK/dV kernels: the NW waves of a
-// work-group each fill LPW 1 KiB pieces of a [64][D] bf16 tile with
+// Tile loader shared by the dQ and dK/dV kernels: NW waves each fill LPW
+// 1 KiB pieces of a [ROWS][D] bf16 tile with
 // global_load_lds_dwordx4 (lane l fills bytes [16 l, 16 l + 16) after the
 // wave-uniform base in M0), choosing each lane's source chunk so that the
 // tile lands swizzled; rows past N are clamped to row N-1.
-template <int D, int NW>
+template <int D, int NW, int ROWS = 64>
 struct TileLoader {
-  static constexpr int TILE = 64 * D;
+  static constexpr int TILE = ROWS * D;
   static constexpr int LPW = TILE * 2 / 1024 / NW;
   static_assert(LPW >= 1 && LPW * 1024 * NW == TILE * 2, "tile must split into 1 KiB per load");
   int row[LPW];
@@ -130,11 +136,11 @@ struct TileLoader {
     }
     lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wave * LPW * 1024));
   }
-  // rows row0 .. row0+63 of the tensor at src (element (row, 0) = src + row*tok)
+  // rows row0 .. row0+ROWS-1 of the tensor at src (element (row, 0) = src + row*tok)
   __device__ void load(const __bf16* src, long long tok, unsigned lds_buf, int row0, int N) const {
     const unsigned la0 = lds_buf + lds_wave;
     const __bf16* base = src + (long long)row0 * tok;
-    if (row0 + 64 <= N) {
+    if (row0 + ROWS <= N) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
@@ -154,6 +160,28 @@ struct TileLoader {
 };
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Work-group -> (head, tile) order that keeps each head on one XCD: the
+// hardware deals consecutive work-groups round-robin to the 8 XCDs (each
+// with its own L2), so work-group L runs on XCD L % 8; giving XCD x the
+// contiguous logical range [x G/8, (x+1) G/8) puts all tiles of a head on
+// one L2, which then serves the K/V (or Q/dO) tiles every work-group of
+// that head streams.
+__device__ __forceinline__ int xcd_order(int L) {
+  const int total = gridDim.x;
+  if ((total & 7) != 0) return L;
+  return (L & 7) * (total >> 3) + (L >> 3);
+}
+
+// Ordinary global loads issued before the tile loop must complete before
+// it: the compiler's own wait for a value loaded earlier counts every
+// outstanding vector-memory load, the direct-to-LDS tile loads included,
+// so a first use inside the loop would wait for the next tile as well.
+// An empty asm that reads the registers moves that wait here.
+template <typename T>
+__device__ __forceinline__ void loaded(const T& x) {
+  asm volatile("" ::"v"(x));
+}
 
 // Per-lane element offsets of the transposing reads of a swizzled [rows][D]
 // tile that give a lane (m = ln of a 32-wide column block db, h = lh) the
@@ -226,8 +254,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  const int bh = blockIdx.x / p.n_tiles;
-  const int qt = p.n_tiles - 1 - (blockIdx.x - bh * p.n_tiles);   // longest first
+  const int L = xcd_order(blockIdx.x);
+  const int bh = L / p.n_tiles;
+  const int qt = p.n_tiles - 1 - (L - bh * p.n_tiles);   // longest first
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -258,6 +287,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   const float lse2 = p.lse[(long long)bh * N + qr] * kLog2e;
   const float dd = p.delta[(long long)bh * N + qr];
   const float c = p.c;
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    loaded(qf[ks]);
+    loaded(gf[ks]);
+  }
+  loaded(lse2);
+  loaded(dd);
 
   const int n_kv_all = (N + BC - 1) / BC;
   int wg_tiles = n_kv_all;
@@ -378,8 +414,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  const int bh = blockIdx.x / p.n_ktiles;
-  const int kt = blockIdx.x - bh * p.n_ktiles;   // causal: low key tiles see the most queries
+  const int L = xcd_order(blockIdx.x);
+  const int bh = L / p.n_ktiles;
+  const int kt = L - bh * p.n_ktiles;   // causal: low key tiles see the most queries
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -406,6 +443,11 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       kf[i] = __builtin_bit_cast(bf16x8, ks[2 * i]);
       if constexpr (DK) vf[i] = __builtin_bit_cast(bf16x8, vs[2 * i]);
     }
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) {
+      loaded(kf[i]);
+      if constexpr (DK) loaded(vf[i]);
+    }
   }
   const float c = p.c;
 
@@ -418,12 +460,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const unsigned lds_g = (unsigned)(size_t)((ATTN_LDS __bf16*)gs_base);
   const float* __restrict__ lse_h = p.lse + (long long)bh * N;
   const float* __restrict__ del_h = p.delta + (long long)bh * N;
-  // lse (log2 units) and D of the tile's 64 query rows, by wave 0
-  auto load_rows = [&](int qt0, int buf) {
+  // lse (log2 units) and D of the tile's 64 query rows, by wave 0: loaded
+  // with the tile, written to LDS once the tile's loads have completed
+  float row_lse = 0.f, row_del = 0.f;
+  auto load_rows = [&](int qt0) {
     if (wave == 0) {
       const int r = min(qt0 + lane, N - 1);
-      rowv[buf][0][lane] = lse_h[r] * kLog2e;
-      rowv[buf][1][lane] = del_h[r];
+      row_lse = lse_h[r];
+      row_del = del_h[r];
+    }
+  };
+  auto store_rows_lds = [&](int buf) {
+    if (wave == 0) {
+      rowv[buf][0][lane] = row_lse * kLog2e;
+      rowv[buf][1][lane] = row_del;
     }
   };
 
@@ -443,9 +493,10 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   if (first < n_q_all) {
     ld.load(qg, tok, lds_q, first * BQ, N);
     ld.load(gg, tok, lds_g, first * BQ, N);
-    load_rows(first * BQ, 0);
+    load_rows(first * BQ);
   }
   wait_vmem();
+  if (first < n_q_all) store_rows_lds(0);
   __syncthreads();
 
   for (int j = first; j < n_q_all; ++j) {
@@ -454,7 +505,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       const unsigned nb = (unsigned)((buf ^ 1) * TILE * 2);
       ld.load(qg, tok, lds_q + nb, (j + 1) * BQ, N);
       ld.load(gg, tok, lds_g + nb, (j + 1) * BQ, N);
-      load_rows((j + 1) * BQ, buf ^ 1);
+      load_rows((j + 1) * BQ);
     }
     const int qt0 = j * BQ;
     // the wave's keys see this tile unless all its queries precede them
@@ -523,6 +574,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
       }
     }
     wait_vmem();
+    if (j + 1 < n_q_all) store_rows_lds(buf ^ 1);
     __syncthreads();
   }
 
