@@ -12,8 +12,10 @@ margin of about 3.
 
 Cases: ragged and degenerate shapes (N = 17, 257, 300, 1000; grids that are
 not a multiple of 8), both head dimensions, both masks, a negative and a
-zero scale, a 2048-token case, untouched guard bands around every gradient,
-and bitwise determinism of two identical calls.
+zero scale, a 2048-token case, the long8k workload at full size (B = 2,
+H = 16, N = 8192, d = 128, causal, as the benchmark times it) checked on two
+whole heads, untouched guard bands around every gradient, and bitwise
+determinism of two identical calls.
 """
 
 import numpy as np
@@ -21,9 +23,9 @@ import pytest
 import torch
 
 import exact_attention_tile_amd as eat
-from oracle import attention_backward, bf16_bits_to_float64
+from oracle import attention_backward, attention_backward_head, bf16_bits_to_float64
 from parity_common import SENTINEL_BF16, dev_u16, require_gpu
-from workloads import Workload, make_dout, make_inputs
+from workloads import WORKLOADS, Workload, make_dout, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -113,3 +115,24 @@ def test_backward_bitwise_deterministic():
     _, b2 = run_bwd(inp, dob, 2, 2, 700, 128, True, w.scale)
     for x, y in zip(b1, b2):
         assert torch.equal(x, y)
+
+
+def test_backward_full_size_sampled_heads():
+    w = WORKLOADS["long8k"]
+    B, H, N, d, causal = w.B, w.H, w.N, w.d, True
+    inp, dob = make_inputs(w), make_dout(w)
+    grads, _ = run_bwd(inp, dob, B, H, N, d, causal, w.scale)
+    q, k, v = (bf16_bits_to_float64(inp[x]) for x in ("q", "k", "v"))
+    do = bf16_bits_to_float64(dob)
+    for b, h in ((0, 3), (1, 12)):
+        ref = attention_backward_head(q[b, :, h], k[b, :, h], v[b, :, h], do[b, :, h], w.scale,
+                                      causal)
+        for name, g, r in zip(("dq", "dk", "dv"), grads, ref):
+            diff = g[b, :, h] - r
+            max_rel = float(np.abs(diff).max()) / max(float(np.abs(r).max()), 1e-30)
+            rel_rms = float(np.sqrt((diff ** 2).sum() / (r ** 2).sum()))
+            msg = "long8k b=%d h=%d %s: rel_rms=%.3e max_abs/max_ref=%.3e" % (b, h, name, rel_rms,
+                                                                             max_rel)
+            print(msg, flush=True)
+            assert rel_rms <= BWD_RELRMS, msg
+            assert max_rel <= BWD_MAXABS_REL, msg
