@@ -89,16 +89,50 @@ __device__ __forceinline__ bool seq_view(const FwdParams& p, int D, int b, int h
 //
 // Variable-length calls order the work differently: sequence lengths vary,
 // so a contiguous run of heads per XCD would give one XCD all of a long
-// sequence.  Instead (batch, head) unit bh goes to XCD bh % 8 -- every XCD
-// gets the same share of every sequence and a head's K/V stay in one L2 --
-// and each XCD runs its units query-tile-major, last (longest) tiles first;
-// work-groups past the end of a short sequence exit at once.
+// sequence.  Instead every XCD gets the same share of every sequence: with H
+// a multiple of 8, XCD x takes heads x, x+8, ... of each sequence.  It runs
+// them sequence by sequence, longest sequence first (ranked on the device
+// from the offsets), a sequence's heads one after the other and a head's
+// query tiles last (longest) first.  So the XCD's CUs share one or two heads'
+// K/V in L2 at a time, and the last work-groups are the short ones.  Other
+// shapes send unit bh to XCD bh % 8 and run query-tile-major.  Work-groups
+// past the end of a short sequence exit at once.
+//
+// The sequence of rank r (by length, longest first, ties by index) of a
+// batch of B <= 128 sequences; each lane ranks up to two candidates.
+__device__ __forceinline__ int seq_by_rank(const int* cu, int B, int r) {
+  const int lane = threadIdx.x & 63;
+  for (int c0 = 0; c0 < B; c0 += 64) {
+    const int b = c0 + lane;
+    int rank = -1;
+    if (b < B) {
+      const int len = cu[b + 1] - cu[b];
+      rank = 0;
+      for (int i = 0; i < B; ++i) {
+        const int li = cu[i + 1] - cu[i];
+        rank += (li > len) || (li == len && i < b);
+      }
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(rank == r);
+    if (hit) return c0 + __builtin_ctzll(hit);
+  }
+  return 0;   // unreachable: the ranks are a permutation of 0 .. B-1
+}
+
 __device__ __forceinline__ void block_to_work(const FwdParams& p, int& bh, int& qt) {
   int total = gridDim.x;
   int L = blockIdx.x;
   if (p.cu) {
     const int BH = p.B * p.H;
-    if ((BH & 7) == 0) {
+    if ((p.H & 7) == 0 && p.B <= 128) {
+      const int hx = p.H >> 3;                     // heads per XCD per sequence
+      const int k = L >> 3;
+      const int j = k / p.n_qtiles;
+      qt = p.n_qtiles - 1 - (k - j * p.n_qtiles);
+      const int r = j / hx;
+      const int b = seq_by_rank(p.cu, p.B, r);
+      bh = b * p.H + (L & 7) + 8 * (j - r * hx);
+    } else if ((BH & 7) == 0) {
       const int per = BH >> 3;
       const int k = L >> 3;
       const int t = k / per;
