@@ -66,10 +66,11 @@ __device__ __forceinline__ int v_row_key(int r) {
   return (r & ~63) + 8 * ((r >> 2) & 7) + 4 * ((r >> 5) & 1) + (r & 3);
 }
 
-__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
+__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d, int old) {
   // the untouched half of the first conversion's destination is written by
-  // the second, so its old value may be anything: reuse a's register
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_bit_cast(int, a), false);
+  // the second, so its old value may be anything: pass the dead word the
+  // result replaces, so that the packs land in place
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -350,7 +351,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
         const int kb = 2 * kk + half;
 #pragma unroll
         for (int g = 0; g < 4; ++g)
-          w[4 * half + g] = pack_fp8x4(s[kb][4 * g], s[kb][4 * g + 1], s[kb][4 * g + 2], s[kb][4 * g + 3]);
+          w[4 * half + g] = pack_fp8x4(s[kb][4 * g], s[kb][4 * g + 1], s[kb][4 * g + 2], s[kb][4 * g + 3],
+                                       pf[kk][4 * half + g]);
       }
       pf[kk] = w;
     }
