@@ -41,7 +41,8 @@ METRIC_FWD2 = ("attn fwd fp8 two-pass TFLOPS (4BHN²d, causal halved; the row-ma
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
-KERNEL_SOURCES = {"bf16": ("attn_fwd_bf16.hip", "attn_kernels.hpp", "attn_api.cpp"),
+KERNEL_SOURCES = {"quant": ("attn_quant.hip", "attn_kernels.hpp", "attn_api.cpp"),
+                  "bf16": ("attn_fwd_bf16.hip", "attn_kernels.hpp", "attn_api.cpp"),
                   "fp8": ("attn_fwd_fp8.hip", "attn_kernels.hpp", "attn_api.cpp")}
 
 
@@ -56,11 +57,13 @@ def kernel_source_hash(dtype):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, dtype, causal):
-    """HBM bytes per launch from the committed rocprofv3 counter runs
-    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a plain
-    copy), if they were taken on the current kernel sources; else None."""
-    key = "%s_%s" % (workload, "causal" if causal else "noncausal")
+def measured_traffic(workload, dtype, causal, key=None):
+    """HBM bytes per launch (per step for the quantiser) from the committed
+    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by what it
+    reads for a plain copy), if they were taken on the current kernel
+    sources; else None."""
+    if key is None:
+        key = "%s_%s" % (workload, "causal" if causal else "noncausal")
     try:
         with open(TRAFFIC_FILE) as f:
             for line in f:
@@ -173,7 +176,8 @@ def quant_line(args, w, ms_per_step, avg_launch_ms, src_elems):
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "pass": "quant",
                    "rotation": "Q and K (random Hadamard), V plain"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(w.name, "quant", False, key=w.name + "_quant"),
                      "kernel_avg_ms": round(avg_launch_ms, 4)},
     }
     if not args.no_cpu_baseline:
