@@ -338,6 +338,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
       const __bf16* vt = vs_base + (j & 1) * TILE;
       const int kv0 = j * BC;
       f32x16 s[NKB], dp[NKB];
+      // the matrix-core sections raise the wave's issue priority, so that
+      // the partner wave's vector work fills the slots around its MFMAs
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -348,6 +351,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16{} : dp[kb], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff off - 4*lh <= lim
       const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
       const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
@@ -371,6 +375,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
           dsf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
         }
       }
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
@@ -379,6 +384,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], acc[db], 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     wait_vmem();
     __syncthreads();
