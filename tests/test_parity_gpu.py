@@ -8,6 +8,7 @@ oracle on the same seeded inputs.
   and partial query tiles, grids that are not a multiple of 8) against the
   full oracle, both dtypes, both modes;
 * negative and zero scale;
+* a 65536-token causal context (both dtypes, 256 sampled rows per head);
 * bitwise determinism of two identical calls, and untouched guard bands
   around O and LSE in every run.
 Tolerances are in parity_common.py.
@@ -109,3 +110,17 @@ def test_bitwise_deterministic(dtype):
     b = _run(w, inp, True)
     assert torch.equal(a.o_raw, b.o_raw)
     assert torch.equal(a.l_raw, b.l_raw)
+
+
+# ---------------------------------------------------------------------------
+# a context longer than any benchmark workload (64-bit offsets, many tiles)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_long_context_64k(dtype):
+    w = Workload("ctx64k", 92, 1, 2, 65536, 128, dtype, (True,), outliers=dtype == "fp8")
+    inp = make_inputs(w)
+    out = _run(w, inp, True)
+    rows = sample_rows(w, count=256)
+    ro, rl = reference(inp, dtype, True, w.scale, rows=rows)
+    _check(w, inp, out, ro, rl, True, w.scale, "ctx64k %s" % dtype, rows=rows)
