@@ -16,6 +16,15 @@ throughput target is stated for.  Other workloads (--workload) are for
 exploration; the parity tests cover all of them.
 
 TFLOPS = 4*B*H*N^2*d (halved when causal) / time per step.
+
+Other passes (--pass), each timed the same way with its own JSON line:
+  fwd2   the two-pass fp8 forward (attn_fwd_fp8_2pass), fp8 workloads;
+  bwd    the backward pass (attn_bwd), bf16 workloads, TFLOPS counted as
+         2.5 x the forward's;
+  quant  the E4M3 quantisation of Q, K (rotated) and V (attn_fp8_quantize),
+         fp8 workloads, GB/s of algorithmic bytes against the HBM peak.
+Each line carries the oracle timed on the host beside it (cpu_baseline),
+unless --no-cpu-baseline.
 """
 
 import argparse
@@ -161,6 +170,39 @@ def cpu_baseline(w, inp, causal, budget_s=12.0):
     }
 
 
+def bwd_cpu_baseline(w, inp, dout_bits, causal, budget_s=12.0):
+    """The gradient oracle, as it stands, on whole (batch, head) problems of
+    the same workload taken in order until about ``budget_s`` seconds have
+    passed (at least one), counted with the metric's 2.5 x 4 d N^2 per head
+    (halved when causal)."""
+    from oracle import attention_backward_head, bf16_bits_to_float64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    per_head = 2.5 * 4.0 * w.d * w.N * w.N / (2.0 if causal else 1.0)
+    done = 0
+    t0 = time.perf_counter()
+    for (b, h) in heads:
+        q, k, v, do = (bf16_bits_to_float64(x[b, :, h, :]) for x in
+                       (inp["q"], inp["k"], inp["v"], dout_bits))
+        attention_backward_head(q, k, v, do, w.scale, causal)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": per_head * done / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": "fp64 NumPy gradient oracle on %d of %d whole (batch, head) problems "
+                  "(N=%d, d=%d, %.1f s)" % (done, len(heads), w.N, w.d, dt),
+    }
+
+
 def quant_line(args, w, ms_per_step, avg_launch_ms, src_elems):
     """The JSON line of --pass quant: bytes are algorithmic (each bf16 input
     element read once, each code written once); the second read pass of the
@@ -300,7 +342,8 @@ def main():
         from workloads import make_dout
         step()                                     # O and lse of the forward
         torch.cuda.synchronize()
-        do = dev16(make_dout(w))
+        do_bits = make_dout(w)
+        do = dev16(do_bits)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         delta = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
 
@@ -406,6 +449,8 @@ def main():
         out["metric"] = METRIC_FWD2
     if not args.no_cpu_baseline and args.which in ("fwd", "fwd2"):
         out["cpu_baseline"] = cpu_baseline(w, inp, causal)
+    if not args.no_cpu_baseline and args.which == "bwd":
+        out["cpu_baseline"] = bwd_cpu_baseline(w, inp, do_bits, causal)
     print(json.dumps(out), flush=True)
 
 
