@@ -53,6 +53,7 @@
 namespace attn {
 
 constexpr float kTauBf16 = 8.0f;  // p <= 256: exact range for bf16 / fp32
+constexpr float kPMaxBf16 = 256.0f;   // 2^kTauBf16
 
 // 16-byte-chunk XOR swizzles of the row-major [BC][D] LDS tiles.
 //  K: a ds_read_b128 A-operand read has 16 lanes on 16 consecutive rows at
@@ -268,8 +269,62 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, row max, gated rescale
-  // of m_ref / l / O, exponentials -> pf
+  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, gated rescale of
+  // m_ref / l / O, exponentials -> pf.
+  //
+  // p = exp2(s c - m_ref) of the tile, rounded to bf16 into pf, and two
+  // partial row sums t of the fp32 p (this lane-half's keys).  s is kept.
+  auto exponentials = [&](float* t) {
+    const float neg_m = -m_ref;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = half * 8 + 2 * i;
+          const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
+          const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, neg_m));
+          w[i] = pack_bf16x2(e0, e1);
+          if (kb == 0 && half == 0 && i == 0) {
+            t[0] = e0;
+            t[1] = e1;
+          } else {
+            t[0] += e0;
+            t[1] += e1;
+          }
+        }
+        pf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+        // the packs are used here, so the compiler does not sink them below
+        // the rescale branch that follows (which would keep every p live
+        // across it)
+        asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
+      }
+    }
+  };
+  // Row maximum and gated rescale: m = max_j s_j c over the tile; where it
+  // exceeds m_ref by more than TAU, m_ref moves to it and l and O are scaled
+  // by exp2(m_ref_old - m).  Afterwards every p of the tile is at most 2^TAU.
+  auto rescale = [&]() {
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+    mx = pair_max(mx);
+    const float mt = mx * c;
+    const bool need = mt > m_ref + kTauBf16;
+    const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
+    m_ref = need ? mt : m_ref;
+    l_part[0] *= alpha;
+    l_part[1] *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto phase_y = [&](auto masked_tag, int kv0) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if constexpr (MASKED) {
@@ -282,42 +337,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
         for (int r = 0; r < 16; ++r)
           if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
     }
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[kb][r]), s[kb][r + 1]);
-    mx = pair_max(mx);
-    const float mt = mx * c;
-    const bool need = mt > m_ref + kTauBf16;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m_ref - mt) : 1.f;
-      m_ref = need ? mt : m_ref;
-      l_part[0] *= alpha;
-      l_part[1] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    // The gate without the row maximum on the common path: the tile's
+    // exponentials are taken against the current m_ref first.  When every
+    // lane's partial sum of its p is at most 2^TAU, so is every p -- and a
+    // maximum more than TAU above m_ref would give a p above 2^TAU -- so no
+    // row needs the rescale and the tile is kept.  Otherwise (also on a
+    // wave's first tile, where m_ref = -inf makes the sums inf or NaN) the
+    // wave takes the row maximum, applies the gate and redoes the tile.
+    float t[2];
+    exponentials(t);
+    if (__builtin_amdgcn_ballot_w64(!(t[0] + t[1] <= kPMaxBf16))) {
+      rescale();
+      exponentials(t);
     }
-    const float neg_m = -m_ref;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 w;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = half * 8 + 2 * t;
-          const float e0 = fast_exp2(__builtin_fmaf(s[kb][r], c, neg_m));
-          const float e1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, neg_m));
-          w[t] = pack_bf16x2(e0, e1);
-          l_part[0] += e0;
-          l_part[1] += e1;
-        }
-        pf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
+    l_part[0] += t[0];
+    l_part[1] += t[1];
   };
 
   // ---- phase loop ------------------------------------------------------------

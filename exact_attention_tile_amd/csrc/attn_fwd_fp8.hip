@@ -292,21 +292,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, row max, gated rescale
-  // of m_ref / l / O, exponentials -> pf
-  auto phase_y = [&](auto masked_tag, int kv0) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
-      // off - 4*lh <= lim
-      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
-    }
-    if constexpr (MODE != 2) {
+  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..): mask, gated rescale of
+  // m_ref / l / O, exponentials -> pf.
+  //
+  // Row maximum and gated rescale: m = max_j s_j c over the tile; where it
+  // exceeds m_ref by more than TAU, m_ref moves to it and l and O are scaled
+  // by exp2(m_ref_old - m), skipped by the whole wave when no row moved.
+  // Afterwards every p' of the tile is at most 2^(TAU+P_OFFSET).  The
+  // two-pass form's first pass keeps only the maximum.
+  auto rescale = [&]() {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -329,45 +323,61 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     }
-    }
-    // p' = exp2(s c - m_ref + P_OFFSET), in place: all FMAs, all
-    // exponentials, then the e4m3 packs (64-key step kk, slot t = 16 (kb & 1)
-    // + r) and the row sums (four chains), so that no instruction waits on
-    // the one just before it
-    const float bias = (MODE == 2 ? kPOffset2 : kPOffset) - m_ref;
+  };
+  // p' = exp2(s c - m_ref + offset) of the tile, rounded to e4m3 into pf
+  // (64-key step kk, slot t = 16 (kb & 1) + r; each pack lands in the P word
+  // it replaces), and four partial row sums t of the fp32 p'.  One 32-key
+  // block at a time: its FMAs, then its exponentials, then packs and sums,
+  // so that no instruction waits on the one just before it.
+  auto exponentials = [&](float* t, float offset) {
+    const float bias = offset - m_ref;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 e;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_fmaf(s[kb][r], c, bias);
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_fmaf(s[kb][r], c, bias);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(e[r]);
+      const int kk = kb >> 1, half = kb & 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(s[kb][r]);
+      for (int g = 0; g < 4; ++g)
+        pf[kk][4 * half + g] =
+            pack_fp8x4(e[4 * g], e[4 * g + 1], e[4 * g + 2], e[4 * g + 3], pf[kk][4 * half + g]);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      i32x8 w;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int kb = 2 * kk + half;
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          w[4 * half + g] = pack_fp8x4(s[kb][4 * g], s[kb][4 * g + 1], s[kb][4 * g + 2], s[kb][4 * g + 3],
-                                       pf[kk][4 * half + g]);
+      for (int r = 0; r < 16; ++r) {
+        if (kb == 0 && r < 4)
+          t[r] = e[r];
+        else
+          t[r & 3] += e[r];
       }
-      pf[kk] = w;
+      // one block's p' live at a time: the scheduler does not interleave
+      // the blocks
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto phase_y = [&](auto masked_tag, int kv0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (MASKED) {
+      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
+      // off - 4*lh <= lim
+      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) l_part[r & 3] += s[kb][r];
-    // interleave: FMAs run 8 ahead of the exponentials that read them
-    // (sched_group_barrier masks: 0x002 VALU, 0x400 transcendental)
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 16 * NKB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        for (int r = 0; r < 16; ++r)
+          if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kb][r] = -__builtin_inff();
     }
+    if constexpr (MODE == 1) {
+      rescale();
+      return;
+    }
+    // the two-pass form's second pass knows the exact row maximum: no
+    // running maximum, no rescale
+    if constexpr (MODE == 0) rescale();
+    float t[4];
+    exponentials(t, MODE == 2 ? kPOffset2 : kPOffset);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l_part[i] += t[i];
   };
 
   // ---- phase loop ------------------------------------------------------------
