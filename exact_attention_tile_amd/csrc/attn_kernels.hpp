@@ -38,7 +38,7 @@ struct FwdParams {
   int total;         // variable-length calls: tokens in the packed tensors
   int maxlen;        // longest sequence (N for fixed-length calls)
   int n_qtiles;      // ceil(maxlen / rows per workgroup)
-  int remap;         // 1: XCD-aware block order (grid size divisible by 8)
+  int remap;         // XCD-aware block order (grid divisible by 8): 1 head-major, 2 tile-major
   float c;           // |scale| * log2(e): scores are kept in log2 units
   unsigned qsign;    // sign-flip mask applied to Q when scale < 0
 };
@@ -85,7 +85,10 @@ __device__ __forceinline__ bool seq_view(const FwdParams& p, int D, int b, int h
 // multiple of 8 the index is first regrouped so that consecutive logical
 // blocks -- the query tiles of one head, which share its K/V -- land on one
 // XCD and share its L2.  Within a head, tiles go longest-first (for causal
-// attention the last query tile sees the most keys).
+// attention the last query tile sees the most keys).  Causal calls with few
+// query tiles per head (remap == 2, chosen by the host) keep each XCD's share
+// of heads but run the longest tile of every head first, then the next
+// longest: the tile lengths then pair up over the XCD's CUs.
 //
 // Variable-length calls order the work differently: sequence lengths vary,
 // so a contiguous run of heads per XCD would give one XCD all of a long
@@ -143,6 +146,16 @@ __device__ __forceinline__ void block_to_work(const FwdParams& p, int& bh, int& 
       qt = p.n_qtiles - 1 - t;
       bh = L - t * BH;
     }
+    return;
+  }
+  if (p.remap == 2) {
+    // XCD x takes heads x*hx .. x*hx+hx-1 (B*H = 8*hx), the longest query
+    // tile of each of them first, then the next longest, ...
+    const int hx = (p.B * p.H) >> 3;
+    const int k = L >> 3;
+    const int t = k / hx;
+    bh = (L & 7) * hx + (k - t * hx);
+    qt = p.n_qtiles - 1 - t;
     return;
   }
   if (p.remap) {
