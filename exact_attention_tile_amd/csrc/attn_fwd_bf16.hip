@@ -354,54 +354,76 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     l_part[1] += t[1];
   };
 
-  // ---- phase loop ------------------------------------------------------------
+  // ---- phase schedule ------------------------------------------------------
   // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
   // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
-  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u in phase 2u (into
-  // buffers last read in phases 2u-2 / 2u-1) and waits for them at the end
-  // of phase 2u+1.
-  if (grp == 1 && wg_tiles > 0) load_k(0);
-  wait_loads();
-  __syncthreads();
-
+  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u at the start of
+  // phase 2u (into buffers last read in phases 2u-2 / 2u-1) and waits for
+  // them at the end of phase 2u+1.  Every wave passes the same number of
+  // phase barriers, 2 * wg_tiles + 2.
+  //
+  // A wave with T = wv_tiles tiles runs X_{-1} (S of tile 0 only), Y_{-1},
+  // then X_j (both products) and Y_j for j = 0 .. T-2, then X_{T-1} (P.V
+  // only), and idles to the last phase.  Only the wave's last tile can need
+  // the mask (the causal diagonal, a ragged end), so the tiles before the
+  // first masked one run in a loop without it.
   using T_ = std::true_type;
   using F_ = std::false_type;
   const int n_phases = 2 * wg_tiles + 2;
-  for (int ph = 0; ph < n_phases; ++ph) {
+  int ph = 0;
+  auto start_phase = [&]() {
     if (grp == 1 && (ph & 1) == 0) {
-      const int u = ph >> 1;
+      // every wave counts the same phases; an SGPR for the loads' addresses
+      const int u = __builtin_amdgcn_readfirstlane(ph) >> 1;
       if (u + 1 < wg_tiles) load_k(u + 1);
       if (u < wg_tiles) load_v(u);
     }
-    const int q = ph - grp;
-    if (q >= 0) {
-      if ((q & 1) == 0) {
-        const int j = (q >> 1) - 1;
-        const bool qk = j + 1 < wv_tiles;
-        const bool pv = j >= 0 && j < wv_tiles;
-        const __bf16* kt = ks_base + ((j + 1) & 1) * TILE;
-        const __bf16* vt = vs_base + (j & 1) * TILE;
-        if (qk && pv)
-          phase_x(T_{}, T_{}, kt, vt);
-        else if (qk)
-          phase_x(T_{}, F_{}, kt, vt);
-        else if (pv)
-          phase_x(F_{}, T_{}, kt, vt);
-      } else {
-        const int j = (q - 3) / 2;
-        if (j + 1 < wv_tiles) {
-          const int kv0 = (j + 1) * BC;
-          const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-          if (masked)
-            phase_y(T_{}, kv0);
-          else
-            phase_y(F_{}, kv0);
-        }
-      }
-    }
+  };
+  auto end_phase = [&]() {
     if (grp == 1 && (ph & 1) == 1) wait_loads();
     __syncthreads();
+    ++ph;
+    start_phase();
+  };
+  auto kt_of = [&](int j) { return ks_base + ((j + 1) & 1) * TILE; };   // K tile of X_j
+  auto vt_of = [&](int j) { return vs_base + (j & 1) * TILE; };         // V tile of X_j
+
+  if (grp == 1 && wg_tiles > 0) load_k(0);
+  wait_loads();
+  __syncthreads();
+  start_phase();
+
+  const int T = wv_tiles;
+  // first tile that needs the mask: the causal diagonal or the ragged end
+  int first_masked = N / BC;
+  if (CAUSAL) first_masked = min(first_masked, (qw0 + 1) / BC);
+  if (grp == 1) end_phase();
+  if (T > 0) {
+    phase_x(T_{}, F_{}, kt_of(-1), vt_of(-1));
+    end_phase();
+    if (first_masked <= 0)
+      phase_y(T_{}, 0);
+    else
+      phase_y(F_{}, 0);
+    end_phase();
+    const int t_plain = min(first_masked, T);
+    int t = 1;
+    for (; t < t_plain; ++t) {          // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
+      phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
+      end_phase();
+      phase_y(F_{}, t * BC);
+      end_phase();
+    }
+    for (; t < T; ++t) {                // the masked tail
+      phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
+      end_phase();
+      phase_y(T_{}, t * BC);
+      end_phase();
+    }
+    phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));
+    end_phase();
   }
+  while (ph < n_phases) end_phase();
 
   // ---- epilogue: O = acc / l -> bf16, lse = ln2 * (m_ref + log2 l)
   const float l_tot = pair_sum(l_part[0] + l_part[1]);   // wave-uniform, before any lane test
