@@ -236,7 +236,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   for (int kk = 0; kk < NKK; ++kk) pf[kk] = i32x8{};
 
   // ---- X_j: S^T of tile j+1 (K tile kt) and O^T += V_j^T P_j^T (V tile vt)
-  auto phase_x = [&](auto qk_tag, auto pv_tag, const unsigned char* kt, const unsigned char* vt) {
+  auto phase_x = [&](auto qk_tag, auto pv_tag, const unsigned char* kt, const unsigned char* vt)
+                     __attribute__((always_inline)) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
     // the matrix-core phase issues first on its SIMD; the partner wave's
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   // by exp2(m_ref_old - m), skipped by the whole wave when no row moved.
   // Afterwards every p' of the tile is at most 2^(TAU+P_OFFSET).  The
   // two-pass form's first pass keeps only the maximum.
-  auto rescale = [&]() {
+  auto rescale = [&]() __attribute__((always_inline)) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -329,7 +330,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   // it replaces), and four partial row sums t of the fp32 p'.  One 32-key
   // block at a time: its FMAs, then its exponentials, then packs and sums,
   // so that no instruction waits on the one just before it.
-  auto exponentials = [&](float* t, float offset) {
+  auto exponentials = [&](float* t, float offset) __attribute__((always_inline)) {
     const float bias = offset - m_ref;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto phase_y = [&](auto masked_tag, int kv0) {
+  auto phase_y = [&](auto masked_tag, int kv0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if constexpr (MASKED) {
       // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
@@ -380,54 +381,101 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     for (int i = 0; i < 4; ++i) l_part[i] += t[i];
   };
 
-  // ---- phase loop ------------------------------------------------------------
+  // ---- phase schedule ------------------------------------------------------
   // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
   // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
   // 2t+3 (from buffer t&1).  Group A loads K_{u+1} and V_u at the start of
   // its matrix-core phase 2u (into buffers last read in phases 2u-2 / 2u-1)
-  // and waits for them at the end of phase 2u+1.
+  // and waits for them at the end of phase 2u+1.  Every wave passes the same
+  // number of phase barriers, 2 * wg_tiles + 2.
+  //
+  // A wave with T = wv_tiles tiles runs X_{-1} (S of tile 0 only), Y_{-1},
+  // then X_j (both products; S only in the row-maximum pass) and Y_j for
+  // j = 0 .. T-2, then X_{T-1} (P.V only), and idles to the last phase.
+  // Only the wave's last tile can need the mask (the causal diagonal, a
+  // ragged end), so the tiles before the first masked one run in a loop
+  // without it.  The two groups run separate copies of the schedule, so
+  // group A's loads and waits sit at fixed points of its phases.
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  using PV_ = std::integral_constant<bool, MODE != 1>;
+  const int n_phases = 2 * wg_tiles + 2;
+  auto loads_for = [&](int u) {
+    u = __builtin_amdgcn_readfirstlane(u);    // an SGPR for the loads' addresses
+    if (u + 1 < wg_tiles) load_k(u + 1);
+    if (MODE != 1 && u < wg_tiles) load_v(u);
+  };
+  auto kt_of = [&](int j) { return ks_base + ((j + 1) & 1) * TILE; };   // K tile of X_j
+  auto vt_of = [&](int j) { return vs_base + (j & 1) * TILE; };         // V tile of X_j
+
   if (grp == 0 && wg_tiles > 0) load_k(0);
   wait_loads();
   __syncthreads();
 
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  const int n_phases = 2 * wg_tiles + 2;
-  for (int ph = 0; ph < n_phases; ++ph) {
-    if (grp == 0 && (ph & 1) == 0) {
-      const int u = ph >> 1;
-      if (u + 1 < wg_tiles) load_k(u + 1);
-      if (MODE != 1 && u < wg_tiles) load_v(u);
+  const int T = wv_tiles;
+  // first tile that needs the mask: the causal diagonal or the ragged end
+  int first_masked = N / BC;
+  if (CAUSAL) first_masked = min(first_masked, (qw0 + 1) / BC);
+  const int t_plain = min(first_masked, T);
+  auto schedule = [&](auto loader_tag) __attribute__((always_inline)) {
+    constexpr bool LOADER = decltype(loader_tag)::value;   // group A
+    int ph = 0;
+    // X phases start with group A's loads, Y phases end with its wait
+    auto x_start = [&]() {
+      if constexpr (LOADER) loads_for(ph >> 1);
+    };
+    auto y_end = [&]() {
+      if constexpr (LOADER) wait_loads();
+      __syncthreads();
+      ++ph;
+    };
+    auto x_end = [&]() {
+      __syncthreads();
+      ++ph;
+    };
+    if constexpr (!LOADER) x_end();               // group B starts one phase later
+    if (T > 0) {
+      x_start();
+      phase_x(T_{}, F_{}, kt_of(-1), vt_of(-1));
+      x_end();
+      if (first_masked <= 0)
+        phase_y(T_{}, 0);
+      else
+        phase_y(F_{}, 0);
+      y_end();
+      int t = 1;
+      for (; t < t_plain; ++t) {        // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
+        x_start();
+        phase_x(T_{}, PV_{}, kt_of(t - 1), vt_of(t - 1));
+        x_end();
+        phase_y(F_{}, t * BC);
+        y_end();
+      }
+      for (; t < T; ++t) {              // the masked tail
+        x_start();
+        phase_x(T_{}, PV_{}, kt_of(t - 1), vt_of(t - 1));
+        x_end();
+        phase_y(T_{}, t * BC);
+        y_end();
+      }
+      x_start();
+      if constexpr (MODE != 1) phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));
+      x_end();
     }
-    const int q = ph - grp;
-    if (q >= 0) {
-      if ((q & 1) == 0) {
-        const int j = (q >> 1) - 1;
-        const bool qk = j + 1 < wv_tiles;
-        const bool pv = MODE != 1 && j >= 0 && j < wv_tiles;
-        const unsigned char* kt = ks_base + ((j + 1) & 1) * TILE;
-        const unsigned char* vt = vs_base + (j & 1) * TILE;
-        if (qk && pv)
-          phase_x(T_{}, T_{}, kt, vt);
-        else if (qk)
-          phase_x(T_{}, F_{}, kt, vt);
-        else if (pv)
-          phase_x(F_{}, T_{}, kt, vt);
+    // idle to the last phase (group A keeps loading for the other waves)
+    for (; ph < n_phases;) {
+      if (LOADER && (ph & 1) == 0) {
+        x_start();
+        x_end();
       } else {
-        const int j = (q - 3) / 2;
-        if (j + 1 < wv_tiles) {
-          const int kv0 = (j + 1) * BC;
-          const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-          if (masked)
-            phase_y(T_{}, kv0);
-          else
-            phase_y(F_{}, kv0);
-        }
+        y_end();
       }
     }
-    if (grp == 0 && (ph & 1) == 1) wait_loads();
-    __syncthreads();
-  }
+  };
+  if (grp == 0)
+    schedule(T_{});
+  else
+    schedule(F_{});
 
   if constexpr (MODE == 1) {
     if (myq < N && lh == 0) p.lse[sv.lse_base + myq] = m_ref;
