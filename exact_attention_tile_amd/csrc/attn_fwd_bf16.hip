@@ -216,7 +216,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   for (int kk = 0; kk < NKK; ++kk) pf[kk] = bf16x8{};
 
   // ---- X_j: S^T of tile j+1 (K tile kt) and O^T += V_j^T P_j^T (V tile vt)
-  auto phase_x = [&](auto qk_tag, auto pv_tag, const __bf16* kt, const __bf16* vt) {
+  auto phase_x = [&](auto qk_tag, auto pv_tag, const __bf16* kt, const __bf16* vt)
+                     __attribute__((always_inline)) {
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
     // the matrix-core phase issues first on its SIMD; the partner wave's
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   //
   // p = exp2(s c - m_ref) of the tile, rounded to bf16 into pf, and two
   // partial row sums t of the fp32 p (this lane-half's keys).  s is kept.
-  auto exponentials = [&](float* t) {
+  auto exponentials = [&](float* t) __attribute__((always_inline)) {
     const float neg_m = -m_ref;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   // Row maximum and gated rescale: m = max_j s_j c over the tile; where it
   // exceeds m_ref by more than TAU, m_ref moves to it and l and O are scaled
   // by exp2(m_ref_old - m).  Afterwards every p of the tile is at most 2^TAU.
-  auto rescale = [&]() {
+  auto rescale = [&]() __attribute__((always_inline)) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto phase_y = [&](auto masked_tag, int kv0) {
+  auto phase_y = [&](auto masked_tag, int kv0) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     if constexpr (MASKED) {
       // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
@@ -358,32 +359,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
   // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
   // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u at the start of
-  // phase 2u (into buffers last read in phases 2u-2 / 2u-1) and waits for
-  // them at the end of phase 2u+1.  Every wave passes the same number of
-  // phase barriers, 2 * wg_tiles + 2.
+  // its vector phase 2u (into buffers last read in phases 2u-2 / 2u-1) and
+  // waits for them at the end of phase 2u+1.  Every wave passes the same
+  // number of phase barriers, 2 * wg_tiles + 2.
   //
   // A wave with T = wv_tiles tiles runs X_{-1} (S of tile 0 only), Y_{-1},
   // then X_j (both products) and Y_j for j = 0 .. T-2, then X_{T-1} (P.V
   // only), and idles to the last phase.  Only the wave's last tile can need
   // the mask (the causal diagonal, a ragged end), so the tiles before the
-  // first masked one run in a loop without it.
+  // first masked one run in a loop without it.  The two groups run separate
+  // copies of the schedule, so group B's loads and waits sit at fixed points
+  // of its phases.
   using T_ = std::true_type;
   using F_ = std::false_type;
   const int n_phases = 2 * wg_tiles + 2;
-  int ph = 0;
-  auto start_phase = [&]() {
-    if (grp == 1 && (ph & 1) == 0) {
-      // every wave counts the same phases; an SGPR for the loads' addresses
-      const int u = __builtin_amdgcn_readfirstlane(ph) >> 1;
-      if (u + 1 < wg_tiles) load_k(u + 1);
-      if (u < wg_tiles) load_v(u);
-    }
-  };
-  auto end_phase = [&]() {
-    if (grp == 1 && (ph & 1) == 1) wait_loads();
-    __syncthreads();
-    ++ph;
-    start_phase();
+  auto loads_for = [&](int u) {
+    u = __builtin_amdgcn_readfirstlane(u);    // an SGPR for the loads' addresses
+    if (u + 1 < wg_tiles) load_k(u + 1);
+    if (u < wg_tiles) load_v(u);
   };
   auto kt_of = [&](int j) { return ks_base + ((j + 1) & 1) * TILE; };   // K tile of X_j
   auto vt_of = [&](int j) { return vs_base + (j & 1) * TILE; };         // V tile of X_j
@@ -391,39 +384,73 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   if (grp == 1 && wg_tiles > 0) load_k(0);
   wait_loads();
   __syncthreads();
-  start_phase();
 
   const int T = wv_tiles;
   // first tile that needs the mask: the causal diagonal or the ragged end
   int first_masked = N / BC;
   if (CAUSAL) first_masked = min(first_masked, (qw0 + 1) / BC);
-  if (grp == 1) end_phase();
-  if (T > 0) {
-    phase_x(T_{}, F_{}, kt_of(-1), vt_of(-1));
-    end_phase();
-    if (first_masked <= 0)
-      phase_y(T_{}, 0);
-    else
-      phase_y(F_{}, 0);
-    end_phase();
-    const int t_plain = min(first_masked, T);
-    int t = 1;
-    for (; t < t_plain; ++t) {          // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
-      phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
-      end_phase();
-      phase_y(F_{}, t * BC);
-      end_phase();
+  const int t_plain = min(first_masked, T);
+  auto schedule = [&](auto loader_tag) __attribute__((always_inline)) {
+    constexpr bool LOADER = decltype(loader_tag)::value;   // group B
+    int ph = 0;
+    // Y phases start with group B's loads, X phases end with its wait
+    auto y_start = [&]() {
+      if constexpr (LOADER) loads_for(ph >> 1);
+    };
+    auto x_end = [&]() {
+      if constexpr (LOADER) wait_loads();
+      __syncthreads();
+      ++ph;
+    };
+    auto y_end = [&]() {
+      __syncthreads();
+      ++ph;
+    };
+    if constexpr (LOADER) {                       // group B starts one phase later
+      y_start();
+      y_end();
     }
-    for (; t < T; ++t) {                // the masked tail
-      phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
-      end_phase();
-      phase_y(T_{}, t * BC);
-      end_phase();
+    if (T > 0) {
+      phase_x(T_{}, F_{}, kt_of(-1), vt_of(-1));
+      x_end();
+      y_start();
+      if (first_masked <= 0)
+        phase_y(T_{}, 0);
+      else
+        phase_y(F_{}, 0);
+      y_end();
+      int t = 1;
+      for (; t < t_plain; ++t) {        // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
+        phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
+        x_end();
+        y_start();
+        phase_y(F_{}, t * BC);
+        y_end();
+      }
+      for (; t < T; ++t) {              // the masked tail
+        phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
+        x_end();
+        y_start();
+        phase_y(T_{}, t * BC);
+        y_end();
+      }
+      phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));
+      x_end();
     }
-    phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));
-    end_phase();
-  }
-  while (ph < n_phases) end_phase();
+    // idle to the last phase (group B keeps loading for the other waves)
+    for (; ph < n_phases;) {
+      if (LOADER && (ph & 1) == 0) {
+        y_start();
+        y_end();
+      } else {
+        x_end();
+      }
+    }
+  };
+  if (grp == 1)
+    schedule(T_{});
+  else
+    schedule(F_{});
 
   // ---- epilogue: O = acc / l -> bf16, lse = ln2 * (m_ref + log2 l)
   const float l_tot = pair_sum(l_part[0] + l_part[1]);   // wave-uniform, before any lane test
