@@ -51,6 +51,7 @@ struct BwdParams {
   int B, H, N;
   int n_tiles;       // ceil(N / 256): query tiles per head (dQ)
   int n_ktiles;      // ceil(N / 256): key tiles per head (dK/dV)
+  int tile_major;    // 1: tile-major block order (see bwd_work)
   float c;           // scale * log2(e)
   float scale;
 };
@@ -175,6 +176,26 @@ __device__ __forceinline__ int xcd_order(int L) {
   return (L & 7) * (total >> 3) + (L >> 3);
 }
 
+// (batch*head, rank) of work-group L for n tiles per head; rank 0 is the
+// head's longest tile.  Head-major within each XCD (xcd_order), except for
+// causal calls with few tiles per head (tile_major, B*H divisible by 8):
+// their causal tile lengths do not pair up over an XCD's 32 CUs, so each XCD
+// keeps its share of the heads but runs the longest tile of every head
+// first, then the next longest.
+__device__ __forceinline__ void bwd_work(const BwdParams& p, int n, int& bh, int& rank) {
+  const int L = blockIdx.x;
+  if (p.tile_major) {
+    const int hx = (p.B * p.H) >> 3;
+    const int k = L >> 3;
+    rank = k / hx;
+    bh = (L & 7) * hx + (k - rank * hx);
+    return;
+  }
+  const int Lx = xcd_order(L);
+  bh = Lx / n;
+  rank = Lx - bh * n;
+}
+
 // Ordinary global loads issued before the tile loop must complete before
 // it: the compiler's own wait for a value loaded earlier counts every
 // outstanding vector-memory load, the direct-to-LDS tile loads included,
@@ -256,9 +277,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  const int L = xcd_order(blockIdx.x);
-  const int bh = L / p.n_tiles;
-  const int qt = p.n_tiles - 1 - (L - bh * p.n_tiles);   // longest first
+  int bh, rank;
+  bwd_work(p, p.n_tiles, bh, rank);
+  const int qt = p.n_tiles - 1 - rank;   // longest first
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -422,9 +443,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  const int L = xcd_order(blockIdx.x);
-  const int bh = L / p.n_ktiles;
-  const int kt = L - bh * p.n_ktiles;   // causal: low key tiles see the most queries
+  int bh, kt;
+  bwd_work(p, p.n_ktiles, bh, kt);      // causal: low key tiles see the most queries
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -633,9 +653,8 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pp_kernel(BwdParams p) {
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
-  const int L = xcd_order(blockIdx.x);
-  const int bh = L / p.n_ktiles;
-  const int kt = L - bh * p.n_ktiles;   // causal: low key tiles see the most queries
+  int bh, kt;
+  bwd_work(p, p.n_ktiles, bh, kt);      // causal: low key tiles see the most queries
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -915,6 +934,7 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   prm.H = H;
   prm.N = N;
   prm.n_tiles = (N + 255) / 256;
+  prm.tile_major = causal && prm.n_tiles < 32 && (B * H) % 8 == 0;
   prm.scale = scale;
   prm.c = scale * kLog2e;
   if (d == 128) return causal ? launch_bwd_t<128, true>(prm, stream) : launch_bwd_t<128, false>(prm, stream);

@@ -10,8 +10,9 @@ accumulate in fp32; the forward's bf16 O and its lse enter through D and P.
 Summed over many keys the relative RMS error is a few 1e-3; 1e-2 leaves a
 margin of about 3.
 
-Cases: ragged and degenerate shapes (N = 17, 257, 300, 1000; grids that are
-not a multiple of 8), both head dimensions, both masks, a negative and a
+Cases: ragged and degenerate shapes (N = 17, 257, 300, 520, 1000; grids that
+are not a multiple of 8, and head counts B*H divisible by 8, which the short
+causal calls run in tile-major order), both head dimensions, both masks, a negative and a
 zero scale, a 2048-token case, the long8k workload at full size (B = 2,
 H = 16, N = 8192, d = 128, causal, as the benchmark times it) checked on two
 whole heads, untouched guard bands around every gradient, and bitwise
@@ -83,7 +84,9 @@ def check_bwd(inp, do_bits, grads, causal, scale, label):
 
 
 BWD_SHAPES = [(1, 2, 128, 64), (2, 3, 300, 128), (1, 2, 1000, 64), (1, 1, 17, 128),
-              (3, 1, 257, 64), (1, 4, 2048, 128)]
+              (3, 1, 257, 64), (1, 4, 2048, 128),
+              # B*H divisible by 8: the causal calls take the tile-major block order
+              (2, 4, 1000, 64), (1, 8, 520, 128)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
