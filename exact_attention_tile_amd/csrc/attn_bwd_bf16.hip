@@ -348,67 +348,93 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < wg_tiles; ++j) {
+  // one K/V tile of this wave: S^T and dP^T, dS^T, dQ^T += K^T dS^T
+  auto tile = [&](auto masked_tag, int j) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const __bf16* kt = ks_base + (j & 1) * TILE;
+    const __bf16* vt = vs_base + (j & 1) * TILE;
+    const int kv0 = j * BC;
+    f32x16 s[NKB], dp[NKB];
+    // the matrix-core sections raise the wave's issue priority, so that
+    // the partner wave's vector work fills the slots around its MFMAs
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 ka = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
+        const bf16x8 va = *(const bf16x8*)(vt + kb * 32 * D + koff[ks]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16{} : dp[kb], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff off - 4*lh <= lim
+    const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
+    bf16x8 dsf[NKK];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = half * 8 + 2 * t;
+          float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+          float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -lse2));
+          if constexpr (MASKED) {
+            if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p0 = 0.f;
+            if (kb * 32 + 8 * ((r + 1) >> 2) + ((r + 1) & 3) > lim) p1 = 0.f;
+          }
+          w[t] = pack_bf16x2(p0 * (dp[kb][r] - dd), p1 * (dp[kb][r + 1] - dd));
+        }
+        dsf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 a = tr_operand(kt + kk * 16 * D, tro.lo[db], tro.hi[db]);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], acc[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // the next tile's loads (every wave takes part), then this tile
+  auto next_loads = [&](int j) __attribute__((always_inline)) {
+    j = __builtin_amdgcn_readfirstlane(j);    // every wave counts the same tiles; SGPR addresses
     if (j + 1 < wg_tiles) {
       const unsigned nb = (unsigned)(((j + 1) & 1) * TILE * 2);
       ld.load(kg, tok, lds_k + nb, (j + 1) * BC, N);
       ld.load(vg, tok, lds_v + nb, (j + 1) * BC, N);
     }
-    if (j < wv_tiles) {
-      const __bf16* kt = ks_base + (j & 1) * TILE;
-      const __bf16* vt = vs_base + (j & 1) * TILE;
-      const int kv0 = j * BC;
-      f32x16 s[NKB], dp[NKB];
-      // the matrix-core sections raise the wave's issue priority, so that
-      // the partner wave's vector work fills the slots around its MFMAs
-      __builtin_amdgcn_s_setprio(3);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 ka = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
-          const bf16x8 va = *(const bf16x8*)(vt + kb * 32 * D + koff[ks]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], ks == 0 ? f32x16{} : s[kb], 0, 0, 0);
-          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], ks == 0 ? f32x16{} : dp[kb], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-      // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff off - 4*lh <= lim
-      const bool masked = (kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0);
-      const int lim = min(CAUSAL ? myq - kv0 - 4 * lh : 0x7fffffff, N - 1 - kv0 - 4 * lh);
-      bf16x8 dsf[NKK];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 w;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int r = half * 8 + 2 * t;
-            float p0 = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-            float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], c, -lse2));
-            if (masked) {
-              if (kb * 32 + 8 * (r >> 2) + (r & 3) > lim) p0 = 0.f;
-              if (kb * 32 + 8 * ((r + 1) >> 2) + ((r + 1) & 3) > lim) p1 = 0.f;
-            }
-            w[t] = pack_bf16x2(p0 * (dp[kb][r] - dd), p1 * (dp[kb][r + 1] - dd));
-          }
-          dsf[kb * 2 + half] = __builtin_bit_cast(bf16x8, w);
-        }
-      }
-      __builtin_amdgcn_s_setprio(3);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = tr_operand(kt + kk * 16 * D, tro.lo[db], tro.hi[db]);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, dsf[kk], acc[db], 0, 0, 0);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
+  };
+  auto end_tile = [&]() __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();
+  };
+  // Only the wave's last tile can need the mask (the causal diagonal, a
+  // ragged end): the tiles before the first masked one run without it.
+  int first_masked = N / BC;
+  if (CAUSAL) first_masked = min(first_masked, (qw0 + 1) / BC);
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int j = 0;
+  for (const int j_plain = min(first_masked, wv_tiles); j < j_plain; ++j) {
+    next_loads(j);
+    tile(F_{}, j);
+    end_tile();
+  }
+  for (; j < wv_tiles; ++j) {
+    next_loads(j);
+    tile(T_{}, j);
+    end_tile();
+  }
+  for (; j < wg_tiles; ++j) {           // the other waves' tiles: loads and barriers only
+    next_loads(j);
+    end_tile();
   }
 
   if (myq < N) store_rows<NDB>((__bf16*)p.dq + head_base + (long long)myq * tok, acc, p.scale, lh);
