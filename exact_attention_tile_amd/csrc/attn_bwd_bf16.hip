@@ -553,83 +553,119 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   if (first < n_q_all) store_rows_lds(0);
   __syncthreads();
 
-  for (int j = first; j < n_q_all; ++j) {
+  // one query tile j of this wave's keys
+  auto tile = [&](auto masked_tag, int j) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = (j - first) & 1;
-    if (j + 1 < n_q_all) {
-      const unsigned nb = (unsigned)((buf ^ 1) * TILE * 2);
-      ld.load(qg, tok, lds_q + nb, (j + 1) * BQ, N);
-      ld.load(gg, tok, lds_g + nb, (j + 1) * BQ, N);
-      load_rows((j + 1) * BQ);
-    }
     const int qt0 = j * BQ;
-    // the wave's keys see this tile unless all its queries precede them
-    const bool active = kw0 < N && (!CAUSAL || qt0 + BQ - 1 >= kw0);
-    if (active) {
-      const __bf16* qt = qs_base + buf * TILE;
-      const __bf16* gt = gs_base + buf * TILE;
-      const bool masked = (qt0 + BQ > N) || (CAUSAL && qt0 < kw0 + 31);
+    const __bf16* qt = qs_base + buf * TILE;
+    const __bf16* gt = gs_base + buf * TILE;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x8 qa = *(const bf16x8*)(qt + qb * 32 * D + qoff[ks]);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 qa = *(const bf16x8*)(qt + qb * 32 * D + qoff[ks]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s, 0, 0, 0);
+        if constexpr (DK) {
+          const bf16x8 ga = *(const bf16x8*)(gt + qb * 32 * D + qoff[ks]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
+        }
+      }
+      // register r holds query qt0 + 32 qb + 8 (r/4) + 4 lh + r%4 of key mykey
+      bf16x8 pf[2], dsf[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        u32x4 wp, wd;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int rb = 8 * g + 4 * half;                        // registers rb .. rb+3
+          const int qi = 32 * qb + 8 * (rb >> 2) + 4 * lh;        // their first tile row
+          const f32x4 lv = *(const f32x4*)&rowv[buf][0][qi];
+          const f32x4 dv4 = *(const f32x4*)&rowv[buf][1][qi];
+          float pv[4], dsv[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            float pe = fast_exp2(__builtin_fmaf(s[rb + x], c, -lv[x]));
+            if constexpr (MASKED) {
+              const int q = qt0 + qi + x;
+              if (q >= N || (CAUSAL && mykey > q)) pe = 0.f;
+            }
+            pv[x] = pe;
+            dsv[x] = pe * (dp[rb + x] - dv4[x]);
+          }
+          wp[2 * half] = pack_bf16x2(pv[0], pv[1]);
+          wp[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
+          wd[2 * half] = pack_bf16x2(dsv[0], dsv[1]);
+          wd[2 * half + 1] = pack_bf16x2(dsv[2], dsv[3]);
+        }
+        pf[g] = __builtin_bit_cast(bf16x8, wp);
+        dsf[g] = __builtin_bit_cast(bf16x8, wd);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int rowb = (32 * qb + 16 * g) * D;
+          if constexpr (DV) {
+            const bf16x8 ga = tr_operand(gt + rowb, tro.lo[db], tro.hi[db]);
+            dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pf[g], dv[db], 0, 0, 0);
+          }
           if constexpr (DK) {
-            const bf16x8 ga = *(const bf16x8*)(gt + qb * 32 * D + qoff[ks]);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
-          }
-        }
-        // register r holds query qt0 + 32 qb + 8 (r/4) + 4 lh + r%4 of key mykey
-        bf16x8 pf[2], dsf[2];
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          u32x4 wp, wd;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int rb = 8 * g + 4 * half;                        // registers rb .. rb+3
-            const int qi = 32 * qb + 8 * (rb >> 2) + 4 * lh;        // their first tile row
-            const f32x4 lv = *(const f32x4*)&rowv[buf][0][qi];
-            const f32x4 dv4 = *(const f32x4*)&rowv[buf][1][qi];
-            float pv[4], dsv[4];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              float pe = fast_exp2(__builtin_fmaf(s[rb + x], c, -lv[x]));
-              if (masked) {
-                const int q = qt0 + qi + x;
-                if (q >= N || (CAUSAL && mykey > q)) pe = 0.f;
-              }
-              pv[x] = pe;
-              dsv[x] = pe * (dp[rb + x] - dv4[x]);
-            }
-            wp[2 * half] = pack_bf16x2(pv[0], pv[1]);
-            wp[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
-            wd[2 * half] = pack_bf16x2(dsv[0], dsv[1]);
-            wd[2 * half + 1] = pack_bf16x2(dsv[2], dsv[3]);
-          }
-          pf[g] = __builtin_bit_cast(bf16x8, wp);
-          dsf[g] = __builtin_bit_cast(bf16x8, wd);
-        }
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int rowb = (32 * qb + 16 * g) * D;
-            if constexpr (DV) {
-              const bf16x8 ga = tr_operand(gt + rowb, tro.lo[db], tro.hi[db]);
-              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pf[g], dv[db], 0, 0, 0);
-            }
-            if constexpr (DK) {
-              const bf16x8 qa = tr_operand(qt + rowb, tro.lo[db], tro.hi[db]);
-              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[g], dk[db], 0, 0, 0);
-            }
+            const bf16x8 qa = tr_operand(qt + rowb, tro.lo[db], tro.hi[db]);
+            dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[g], dk[db], 0, 0, 0);
           }
         }
       }
     }
+  };
+  // the next tile's loads (every wave takes part) ...
+  auto next_loads = [&](int j) __attribute__((always_inline)) {
+    j = __builtin_amdgcn_readfirstlane(j);    // every wave counts the same tiles; SGPR addresses
+    if (j + 1 < n_q_all) {
+      const unsigned nb = (unsigned)((((j - first) & 1) ^ 1) * TILE * 2);
+      ld.load(qg, tok, lds_q + nb, (j + 1) * BQ, N);
+      ld.load(gg, tok, lds_g + nb, (j + 1) * BQ, N);
+      load_rows((j + 1) * BQ);
+    }
+  };
+  // ... and after the tile, their row values into LDS and the barrier
+  auto end_tile = [&](int j) __attribute__((always_inline)) {
     wait_vmem();
-    if (j + 1 < n_q_all) store_rows_lds(buf ^ 1);
+    if (j + 1 < n_q_all) store_rows_lds(((j - first) & 1) ^ 1);
     __syncthreads();
+  };
+  // Query tiles of this wave's keys, in order: inactive (all queries
+  // precede the keys, causal), masked (the causal diagonal), unmasked,
+  // masked (the ragged end).  The masked test the tiles had, by tile:
+  // (qt0 + BQ > N) or (causal and qt0 < kw0 + 31); active iff kw0 < N and
+  // (not causal or qt0 + BQ - 1 >= kw0).
+  const int n = n_q_all;
+  const int j_act = kw0 >= N ? n : (CAUSAL ? max(first, kw0 / BQ) : first);
+  const int j_um = CAUSAL ? max(j_act, (kw0 + 31 + BQ - 1) / BQ) : j_act;
+  const int seg_b = max(j_act, min(j_um, n));
+  const int seg_c = max(seg_b, min(N / BQ, n));
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int j = first;
+  for (; j < min(j_act, n); ++j) {      // inactive: loads and barriers only
+    next_loads(j);
+    end_tile(j);
+  }
+  for (; j < seg_b; ++j) {
+    next_loads(j);
+    tile(T_{}, j);
+    end_tile(j);
+  }
+  for (; j < seg_c; ++j) {
+    next_loads(j);
+    tile(F_{}, j);
+    end_tile(j);
+  }
+  for (; j < n; ++j) {
+    next_loads(j);
+    tile(T_{}, j);
+    end_tile(j);
   }
 
   if (mykey < N) {
