@@ -53,7 +53,9 @@ def _check(w, inp, out, ro, rl, causal, scale, label, rows=None):
 # ragged / degenerate shapes, full oracle
 # ---------------------------------------------------------------------------
 
-EDGE = [(1, 1, 1), (1, 1, 17), (2, 3, 130), (1, 2, 1000), (1, 5, 300), (3, 1, 257)]
+EDGE = [(1, 1, 1), (1, 1, 17), (2, 3, 130), (1, 2, 1000), (1, 5, 300), (3, 1, 257),
+        # B*H = 8 with 3 query tiles: causal calls take the tile-major block order
+        (2, 4, 700)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
