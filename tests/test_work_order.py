@@ -1,4 +1,4 @@
-"""Fixed-length work order of the forward kernels (attn_kernels.hpp,
+"""Work order and mask segments of the attention kernels. Fixed-length work order of the forward kernels (attn_kernels.hpp,
 block_to_work, with the order the host's plan() picks in attn_api.cpp),
 restated here: every launch index must map to a distinct (batch*head, query
 tile) pair, so that each query tile is computed exactly once."""
@@ -53,3 +53,62 @@ def test_tile_major_order_for_short_causal_calls():
     # long sequences and non-causal calls keep the head-major order
     assert plan_remap(2, 16, 8192, True)[2] == 1
     assert plan_remap(4, 16, 2048, False)[2] == 1
+
+
+# ---------------------------------------------------------------------------
+# Mask segments.  The kernels run the tiles that need no mask through a body
+# without it; the bounds below restate the kernels' formulas and are checked
+# against the per-tile definition of "needs the mask".
+# ---------------------------------------------------------------------------
+
+def _fwd_first_masked(N, BC, causal, qw0):
+    # attn_fwd_bf16.hip / attn_fwd_fp8.hip and the dQ kernel: first key tile
+    # of a wave (32 queries from qw0) that needs the mask
+    fm = N // BC
+    if causal:
+        fm = min(fm, (qw0 + 1) // BC)
+    return fm
+
+
+def _fwd_tile_masked(N, BC, causal, qw0, t):
+    kv0 = t * BC
+    return (kv0 + BC > N) or (causal and kv0 + BC - 1 > qw0)
+
+
+@pytest.mark.parametrize("BC", (64, 128))
+def test_forward_mask_segments(BC):
+    for N in list(range(1, 1200, 7)) + [2048, 8191, 8192, 8193]:
+        n_kv = -(-N // BC)
+        for causal in (False, True):
+            for qw0 in range(0, N, 32):
+                T = min(qw0 + 31, N - 1) // BC + 1 if causal else n_kv
+                fm = _fwd_first_masked(N, BC, causal, qw0)
+                for t in range(T):
+                    assert (t >= fm) == _fwd_tile_masked(N, BC, causal, qw0, t), (N, causal, qw0, t)
+
+
+def test_backward_dkdv_mask_segments():
+    # attn_bwd_bf16.hip, dK/dV kernel: 256 keys per work-group, 32 per wave,
+    # 64-query tiles; segments inactive / masked / unmasked / masked
+    BQ, BK = 64, 256
+    for N in list(range(1, 1500, 11)) + [2048, 8191, 8192, 8193]:
+        n = -(-N // BQ)
+        for causal in (False, True):
+            for kt in range(-(-N // BK)):
+                k0 = kt * BK
+                first = k0 // BQ if causal else 0
+                for wave in range(8):
+                    kw0 = k0 + wave * 32
+                    j_act = n if kw0 >= N else (max(first, kw0 // BQ) if causal else first)
+                    j_um = max(j_act, (kw0 + 31 + BQ - 1) // BQ) if causal else j_act
+                    seg_b = max(j_act, min(j_um, n))
+                    seg_c = max(seg_b, min(N // BQ, n))
+                    for j in range(first, n):
+                        qt0 = j * BQ
+                        active = kw0 < N and ((not causal) or qt0 + BQ - 1 >= kw0)
+                        masked = (qt0 + BQ > N) or (causal and qt0 < kw0 + 31)
+                        if j < min(j_act, n):
+                            got = None
+                        else:
+                            got = not (seg_b <= j < seg_c)
+                        assert got == (masked if active else None), (N, causal, kt, wave, j)
