@@ -1,7 +1,13 @@
-"""Work order and mask segments of the attention kernels. Fixed-length work order of the forward kernels (attn_kernels.hpp,
-block_to_work, with the order the host's plan() picks in attn_api.cpp),
-restated here: every launch index must map to a distinct (batch*head, query
-tile) pair, so that each query tile is computed exactly once."""
+"""Work order and mask segments of the attention kernels, restated here.
+
+Block order: the fixed-length forward kernels (attn_kernels.hpp,
+block_to_work, with the order the host's plan() picks in attn_api.cpp) must
+map every launch index to a distinct (batch*head, query tile) pair, so that
+each query tile is computed exactly once.
+
+Mask segments: the forward, dQ and dK/dV tile loops run the tiles that need
+no mask through a body without it; the segment bounds must agree with the
+per-tile definition of a masked tile."""
 
 import itertools
 
