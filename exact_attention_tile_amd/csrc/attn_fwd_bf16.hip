@@ -475,452 +475,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// d = 128 form on v_mfma_f32_16x16x32_bf16.  Same method, schedule, loads and
-// ping-pong as the kernel above; only the product shape and with it the lane
-// layout change.  Measured beside a softmax wave on the same SIMD, this MFMA
-// shape keeps the matrix cores busier for the same flops than 32x32x16 (it
-// writes a quarter of the accumulator registers per instruction).
-//
-// Lane l = 16 g + n (n = l % 16, g = l / 16).  A wave's 32 queries are two
-// 16-query blocks qb; a 64-key tile is four 16-key blocks kb.
-//   S^T block (kb, qb), register i: key kv0 + 16 kb + 4 g + i, query
-//     qw0 + 16 qb + n.  So a lane holds 16 keys of each of its two queries;
-//     the row max and sum combine the four lane groups g with
-//     permlane32_swap and permlane16_swap.
-//   S^T = K Q^T, k-step ks (32 columns): A = K row 16 kb + n, columns
-//     32 ks + 8 g .. +7 (ds_read_b128); B = Q row qw0 + 16 qb + n, same columns.
-//   O^T += V^T P^T, 32-key step s: B slot t of lane (n, g) holds key
-//     32 s + 4 g + (t & 3) + 16 (t >> 2) -- registers 0..3 of S^T blocks 2s
-//     and 2s+1 -- and A (V^T, 16 columns x the same 8 keys) comes from two
-//     ds_read_b64_tr_b16 at rows 32 s + 4 g .. +3 and 32 s + 16 + 4 g .. +3.
-//   O^T block (db, qb), register i: column 16 db + 4 g + i, query qw0 + 16 qb + n.
-// ---------------------------------------------------------------------------
-// V swizzle of this form: the transposing reads of a wave touch rows r0 .. r0+15
-// at two adjacent 16-byte chunks; chunk ^ 2 (row & 7) spreads them over the
-// banks.  K keeps the 16-row swizzle of the kernel above.
-__device__ __forceinline__ int swz_v16(int row) { return 2 * (row & 7); }
-
-template <bool CAUSAL>
-__global__ __launch_bounds__(512, 1) void attn_fwd_bf16_mf16_kernel(FwdParams p) {
-  constexpr int D = 128, NW = 8, BC = 64;
-  constexpr int BR = NW * 32;            // query rows per work-group
-  constexpr int NKB = BC / 16;           // 16-key blocks per tile
-  constexpr int NQB = 2;                 // 16-query blocks per wave
-  constexpr int NDB = D / 16;            // 16-wide column blocks of the output
-  constexpr int NKS = D / 32;            // k-steps of the QK^T product
-  constexpr int NSS = BC / 32;           // 32-key steps of the P.V product
-  constexpr int TILE = BC * D;           // elements per K or V tile
-
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * 2 * TILE];
-  __bf16* ks_base = smem;                // K tiles: [2][BC][D]
-  __bf16* vs_base = smem + 2 * TILE;     // V tiles: [2][BC][D]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int grp = wave >> 2;             // 0: group A, 1: group B
-  const int n16 = lane & 15;
-  const int g = lane >> 4;
-
-  int bh, qt;
-  block_to_work(p, bh, qt);
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  SeqView sv;
-  if (!seq_view(p, D, b, h, qt * BR, sv)) return;   // whole work-group, before any barrier
-  const int N = sv.N;
-  const long long tok = (long long)p.H * D;       // elements between tokens of Q and O
-  const long long tkv = (long long)p.Hkv * D;     // elements between tokens of K and V
-
-  const int q0 = qt * BR;
-  const int qw0 = q0 + wave * 32;
-  int myq[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) myq[qb] = qw0 + 16 * qb + n16;
-
-  const __bf16* __restrict__ qg = (const __bf16*)p.q + sv.q_base;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + sv.kv_base;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + sv.kv_base;
-
-  // ---- Q^T fragments (B operand): lane (n, g) holds Q[myq[qb]][32 ks + 8 g .. +7]
-  bf16x8 qf[NQB][NKS];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qr = myq[qb] < N ? myq[qb] : N - 1;
-    const u32x4* src = (const u32x4*)(qg + (long long)qr * tok + 8 * g);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 t = src[4 * ks];
-      t ^= p.qsign;
-      qf[qb][ks] = __builtin_bit_cast(bf16x8, t);
-    }
-  }
-
-  // ---- tile range of this work-group and of this wave
-  const int n_kv_all = (N + BC - 1) / BC;
-  int wg_tiles = n_kv_all;
-  int wv_tiles = qw0 < N ? n_kv_all : 0;
-  if (CAUSAL) {
-    const int last_wg = min(q0 + BR - 1, N - 1);
-    wg_tiles = last_wg / BC + 1;
-    if (qw0 < N) wv_tiles = min(qw0 + 31, N - 1) / BC + 1;
-  }
-
-  // ---- tile loader (group B only), as in the kernel above; V under swz_v16
-  constexpr int LPW = TILE * 2 / 1024 / 4;              // loads per B wave per tensor per tile
-  static_assert(LPW * 1024 * 4 == TILE * 2, "tile must split into 1 KiB per load");
-  const int wb = wave & 3;
-  int ld_row[LPW];
-  unsigned kgo[LPW], vgo[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int off = (wb * LPW + i) * 512 + lane * 8;     // element offset in the tile
-    const int row = off / D;
-    const int pc = (off - row * D) / 8;                   // physical 16-byte chunk
-    ld_row[i] = row;
-    kgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_k<D>(row)) * 8) * 2);
-    vgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_v16(row)) * 8) * 2);
-  }
-  const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS __bf16*)ks_base);
-  const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS __bf16*)vs_base);
-  const unsigned lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wb * LPW * 1024));
-  auto load_tile = [&](const unsigned* go, const __bf16* src, unsigned lds_buf, int j) {
-    const int kv0 = j * BC;
-    const unsigned la0 = lds_buf + lds_wave;
-    if (kv0 + BC <= N) {
-      const __bf16* base = src + (long long)kv0 * tkv;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
-                     "v"(go[i]), "s"(base)
-                     : "memory");
-    } else {
-      const __bf16* base = src + (long long)kv0 * tkv;
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const long long back = (long long)(kv0 + ld_row[i] < N ? 0 : kv0 + ld_row[i] - (N - 1)) * tkv;
-        const __bf16* gp = base + (long long)(go[i] / 2) - back;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
-                     "v"(gp)
-                     : "memory");
-      }
-    }
-  };
-  auto load_k = [&](int j) { load_tile(kgo, kg, lds_k + (unsigned)((j & 1) * TILE * 2), j); };
-  auto load_v = [&](int j) { load_tile(vgo, vg, lds_v + (unsigned)((j & 1) * TILE * 2), j); };
-  auto wait_loads = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-
-  // ---- per-lane LDS read offsets (elements)
-  // K A-operand of (kb, ks): row 16 kb + n, chunk 4 ks + g, swizzled by the
-  // row (swz_k<128>(row) = row & 15 = n for every kb)
-  int koff[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = n16 * D + (((4 * ks + g) ^ swz_k<D>(n16)) * 8);
-  // V^T A-operand via the transposing read: in each 16-lane group g, source
-  // lane i reads row 4 g + i / 4 (+ 32 s, + 16 for the second read), columns
-  // 16 db + 4 (i % 4) .. +3.  Rows differ by multiples of 8 between the reads
-  // of a lane, so the swizzle is a per-lane constant.
-  const int vrow_l = 4 * g + (n16 >> 2);
-  const int vsw = swz_v16(vrow_l);
-  int voff[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    const int chunk = 2 * db + ((n16 >> 1) & 1);
-    voff[db] = vrow_l * D + ((chunk ^ vsw) * 8) + (n16 & 1) * 4;
-  }
-
-  // ---- running state (per lane: two queries)
-  f32x4 oacc[NDB][NQB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) oacc[db][qb] = f32x4{};
-  float m_ref[NQB] = {-__builtin_inff(), -__builtin_inff()};
-  float l_part[NQB] = {0.f, 0.f};
-  const float c = p.c;
-  f32x4 s[NKB][NQB];                 // S^T of the tile whose softmax is next
-  bf16x8 pf[NSS][NQB];               // P of the tile whose P.V is next
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) s[kb][qb] = f32x4{};
-#pragma unroll
-  for (int ss = 0; ss < NSS; ++ss)
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) pf[ss][qb] = bf16x8{};
-
-  // combine a per-lane value over the four lane groups g of a query
-  auto quad_max = [](float x) __attribute__((always_inline)) {
-    x = pair_max(x);
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  };
-  auto quad_sum = [](float x) __attribute__((always_inline)) {
-    x = pair_sum(x);
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  };
-
-  // ---- X_j: S^T of tile j+1 (K tile kt) and O^T += V_j^T P_j^T (V tile vt)
-  auto phase_x = [&](auto qk_tag, auto pv_tag, const __bf16* kt, const __bf16* vt)
-                     __attribute__((always_inline)) {
-    constexpr bool QK = decltype(qk_tag)::value;
-    constexpr bool PV = decltype(pv_tag)::value;
-    __builtin_amdgcn_s_setprio(3);
-    if constexpr (QK) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const bf16x8 a = *(const bf16x8*)(kt + kb * 16 * D + koff[ks]);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][ks],
-                                                               ks == 0 ? f32x4{} : s[kb][qb], 0, 0, 0);
-        }
-      }
-    }
-    if constexpr (PV) {
-#pragma unroll
-      for (int ss = 0; ss < NSS; ++ss) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const __bf16* vb = vt + ss * 32 * D + voff[db];
-          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb));
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb + 16 * D));
-          i32x4 w;
-          w[0] = (int)(unsigned short)lo[0] | ((int)(unsigned short)lo[1] << 16);
-          w[1] = (int)(unsigned short)lo[2] | ((int)(unsigned short)lo[3] << 16);
-          w[2] = (int)(unsigned short)hi[0] | ((int)(unsigned short)hi[1] << 16);
-          w[3] = (int)(unsigned short)hi[2] | ((int)(unsigned short)hi[3] << 16);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb)
-            oacc[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[ss][qb], oacc[db][qb], 0, 0, 0);
-        }
-      }
-    }
-    // LDS fragments ahead of the MFMAs that consume them (masks: 0x100 LDS
-    // read, 0x008 MFMA); each fragment feeds two MFMAs
-    if constexpr (QK && PV) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int i = 0; i < NKB * NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < NSS * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // ---- Y_j: softmax of S_{j+1} (keys kv0 ..), as in the kernel above: the
-  // exponentials against the current m_ref first; the row maximum and the
-  // gate only when some lane's partial sum exceeds 2^TAU.
-  auto exponentials = [&](float (*t)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const float neg_m = -m_ref[qb];
-#pragma unroll
-      for (int ss = 0; ss < NSS; ++ss) {
-        u32x4 w;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int kb = 2 * ss + half;
-          const float e0 = fast_exp2(__builtin_fmaf(s[kb][qb][0], c, neg_m));
-          const float e1 = fast_exp2(__builtin_fmaf(s[kb][qb][1], c, neg_m));
-          const float e2 = fast_exp2(__builtin_fmaf(s[kb][qb][2], c, neg_m));
-          const float e3 = fast_exp2(__builtin_fmaf(s[kb][qb][3], c, neg_m));
-          w[2 * half] = pack_bf16x2(e0, e1);
-          w[2 * half + 1] = pack_bf16x2(e2, e3);
-          if (ss == 0 && half == 0) {
-            t[qb][0] = e0 + e2;
-            t[qb][1] = e1 + e3;
-          } else {
-            t[qb][0] += e0 + e2;
-            t[qb][1] += e1 + e3;
-          }
-        }
-        pf[ss][qb] = __builtin_bit_cast(bf16x8, w);
-        asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
-      }
-    }
-  };
-  auto rescale = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        mx = fmaxf(fmaxf(mx, fmaxf(s[kb][qb][0], s[kb][qb][1])), fmaxf(s[kb][qb][2], s[kb][qb][3]));
-      mx = quad_max(mx);
-      const float mt = mx * c;
-      const bool need = mt > m_ref[qb] + kTauBf16;
-      const float alpha = need ? fast_exp2(m_ref[qb] - mt) : 1.f;
-      m_ref[qb] = need ? mt : m_ref[qb];
-      l_part[qb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) oacc[db][qb][r] *= alpha;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto phase_y = [&](auto masked_tag, int kv0) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (MASKED) {
-      // key kv0 + 16 kb + 4 g + i is visible to query myq[qb] iff
-      // 16 kb + i <= lim[qb]
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int lim = min(CAUSAL ? myq[qb] - kv0 - 4 * g : 0x7fffffff, N - 1 - kv0 - 4 * g);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (16 * kb + i > lim) s[kb][qb][i] = -__builtin_inff();
-      }
-    }
-    float t[NQB][2];
-    exponentials(t);
-    const float ts0 = t[0][0] + t[0][1];
-    const float ts1 = t[1][0] + t[1][1];
-    if (__builtin_amdgcn_ballot_w64(!(ts0 <= kPMaxBf16) || !(ts1 <= kPMaxBf16))) {
-      rescale();
-      exponentials(t);
-    }
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) l_part[qb] += t[qb][0] + t[qb][1];
-  };
-  // ---- phase schedule ------------------------------------------------------
-  // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
-  // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
-  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u at the start of
-  // its vector phase 2u (into buffers last read in phases 2u-2 / 2u-1) and
-  // waits for them at the end of phase 2u+1.  Every wave passes the same
-  // number of phase barriers, 2 * wg_tiles + 2.
-  //
-  // A wave with T = wv_tiles tiles runs X_{-1} (S of tile 0 only), Y_{-1},
-  // then X_j (both products) and Y_j for j = 0 .. T-2, then X_{T-1} (P.V
-  // only), and idles to the last phase.  Only the wave's last tile can need
-  // the mask (the causal diagonal, a ragged end), so the tiles before the
-  // first masked one run in a loop without it.  The two groups run separate
-  // copies of the schedule, so group B's loads and waits sit at fixed points
-  // of its phases.
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  const int n_phases = 2 * wg_tiles + 2;
-  auto loads_for = [&](int u) {
-    u = __builtin_amdgcn_readfirstlane(u);    // an SGPR for the loads' addresses
-    if (u + 1 < wg_tiles) load_k(u + 1);
-    if (u < wg_tiles) load_v(u);
-  };
-  auto kt_of = [&](int j) { return ks_base + ((j + 1) & 1) * TILE; };   // K tile of X_j
-  auto vt_of = [&](int j) { return vs_base + (j & 1) * TILE; };         // V tile of X_j
-
-  if (grp == 1 && wg_tiles > 0) load_k(0);
-  wait_loads();
-  __syncthreads();
-
-  const int T = wv_tiles;
-  // first tile that needs the mask: the causal diagonal or the ragged end
-  int first_masked = N / BC;
-  if (CAUSAL) first_masked = min(first_masked, (qw0 + 1) / BC);
-  const int t_plain = min(first_masked, T);
-  auto schedule = [&](auto loader_tag) __attribute__((always_inline)) {
-    constexpr bool LOADER = decltype(loader_tag)::value;   // group B
-    int ph = 0;
-    // Y phases start with group B's loads, X phases end with its wait
-    auto y_start = [&]() {
-      if constexpr (LOADER) loads_for(ph >> 1);
-    };
-    auto x_end = [&]() {
-      if constexpr (LOADER) wait_loads();
-      __syncthreads();
-      ++ph;
-    };
-    auto y_end = [&]() {
-      __syncthreads();
-      ++ph;
-    };
-    if constexpr (LOADER) {                       // group B starts one phase later
-      y_start();
-      y_end();
-    }
-    if (T > 0) {
-      phase_x(T_{}, F_{}, kt_of(-1), vt_of(-1));
-      x_end();
-      y_start();
-      if (first_masked <= 0)
-        phase_y(T_{}, 0);
-      else
-        phase_y(F_{}, 0);
-      y_end();
-      int t = 1;
-      for (; t < t_plain; ++t) {        // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
-        phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
-        x_end();
-        y_start();
-        phase_y(F_{}, t * BC);
-        y_end();
-      }
-      for (; t < T; ++t) {              // the masked tail
-        phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
-        x_end();
-        y_start();
-        phase_y(T_{}, t * BC);
-        y_end();
-      }
-      phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));
-      x_end();
-    }
-    // idle to the last phase (group B keeps loading for the other waves)
-    for (; ph < n_phases;) {
-      if (LOADER && (ph & 1) == 0) {
-        y_start();
-        y_end();
-      } else {
-        x_end();
-      }
-    }
-  };
-  if (grp == 1)
-    schedule(T_{});
-  else
-    schedule(F_{});
-
-  // ---- epilogue: O = acc / l -> bf16, lse = ln2 * (m_ref + log2 l)
-  float l_tot[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) l_tot[qb] = quad_sum(l_part[qb]);   // wave-uniform calls
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    if (myq[qb] < N) {
-      const float inv = 1.f / l_tot[qb];
-      __bf16* og = (__bf16*)p.o + sv.q_base + (long long)myq[qb] * tok;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x2 w;
-        w[0] = pack_bf16x2(oacc[db][qb][0] * inv, oacc[db][qb][1] * inv);
-        w[1] = pack_bf16x2(oacc[db][qb][2] * inv, oacc[db][qb][3] * inv);
-        *(u32x2*)(og + 16 * db + 4 * g) = w;
-      }
-      if (g == 0) p.lse[sv.lse_base + myq[qb]] = (m_ref[qb] + fast_log2(l_tot[qb])) * 0.69314718055994531f;
-    }
-  }
-}
-
-template <bool CAUSAL>
-static hipError_t launch_bf16_mf16_t(const FwdParams& prm, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_bf16_mf16_kernel<CAUSAL>), dim3(grid), dim3(512), 0, stream, prm);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
 // host-side launch helpers (called by the C ABI in attn_api.cpp)
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BC, bool CAUSAL>
@@ -938,13 +492,7 @@ constexpr int kBf16Waves = 8;
 
 int bf16_rows_per_block(int d) { return kBf16Waves * 32; }
 
-// d = 128 on the 16x16x32 form: parity green, measured equal (non-causal) or
-// 1-2% slower (causal long8k) than the 32x32x16 kernel on one box, so off
-constexpr bool kBf16Mf16 = false;
-
 hipError_t launch_bf16(const FwdParams& prm, int d, int causal, int grid, hipStream_t stream) {
-  if (d == 128 && kBf16Mf16)
-    return causal ? launch_bf16_mf16_t<true>(prm, grid, stream) : launch_bf16_mf16_t<false>(prm, grid, stream);
   if (d == 128) {
     return causal ? launch_bf16_t<128, kBf16Waves, 64, true>(prm, grid, stream)
                   : launch_bf16_t<128, kBf16Waves, 64, false>(prm, grid, stream);
