@@ -326,8 +326,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto phase_y = [&](auto masked_tag, int kv0) __attribute__((always_inline)) {
+  auto phase_y = [&](auto masked_tag, int kv0, auto first_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;   // the wave's first tile: m_ref = -inf
     if constexpr (MASKED) {
       // key kv0 + off (off = kb*32 + 8*(r/4) + 4*lh + r%4) is visible iff
       // off - 4*lh <= lim
@@ -342,14 +343,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     // exponentials are taken against the current m_ref first.  When every
     // lane's partial sum of its p is at most 2^TAU, so is every p -- and a
     // maximum more than TAU above m_ref would give a p above 2^TAU -- so no
-    // row needs the rescale and the tile is kept.  Otherwise (also on a
-    // wave's first tile, where m_ref = -inf makes the sums inf or NaN) the
-    // wave takes the row maximum, applies the gate and redoes the tile.
+    // row needs the rescale and the tile is kept.  Otherwise (inf or NaN
+    // sums included) the wave takes the row maximum, applies the gate and
+    // redoes the tile.  A wave's first tile, with no reference yet, takes
+    // the maximum right away.
     float t[2];
-    exponentials(t);
-    if (__builtin_amdgcn_ballot_w64(!(t[0] + t[1] <= kPMaxBf16))) {
+    if constexpr (FIRST) {
+      // no reference yet: the sums would be inf or NaN, so take the maximum
+      // right away
       rescale();
       exponentials(t);
+    } else {
+      exponentials(t);
+      if (__builtin_amdgcn_ballot_w64(!(t[0] + t[1] <= kPMaxBf16))) {
+        rescale();
+        exponentials(t);
+      }
     }
     l_part[0] += t[0];
     l_part[1] += t[1];
@@ -415,23 +424,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       x_end();
       y_start();
       if (first_masked <= 0)
-        phase_y(T_{}, 0);
+        phase_y(T_{}, 0, T_{});
       else
-        phase_y(F_{}, 0);
+        phase_y(F_{}, 0, T_{});
       y_end();
       int t = 1;
       for (; t < t_plain; ++t) {        // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
         phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
         x_end();
         y_start();
-        phase_y(F_{}, t * BC);
+        phase_y(F_{}, t * BC, F_{});
         y_end();
       }
       for (; t < T; ++t) {              // the masked tail
         phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
         x_end();
         y_start();
-        phase_y(T_{}, t * BC);
+        phase_y(T_{}, t * BC, F_{});
         y_end();
       }
       phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));
