@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -440,7 +441,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(w.name, w.dtype, causal),
-                     "kernel_avg_ms": round(avg_launch_ms, 4)},
+                     "kernel_avg_ms": round(avg_launch_ms, 4),
+                     "kernel_median_ms": round(statistics.median(launch_ms), 4),
+                     "kernel_min_ms": round(min(launch_ms), 4)},
     }
     if args.which in ("bwd", "fwd2"):
         out["config"]["pass"] = args.which
