@@ -958,23 +958,19 @@ template <int D, bool CAUSAL>
 static hipError_t launch_bwd_t(BwdParams prm, hipStream_t stream) {
   const long long rows = (long long)prm.B * prm.N * prm.H;
   const int grid_delta = (int)((rows + 15) / 16);
-  hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3(grid_delta), dim3(256), 0, stream, prm);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(attn_bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), stream, prm);
   if (e != hipSuccess) return e;
   const int grid = prm.B * prm.H * prm.n_tiles;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<D, CAUSAL>), dim3(grid), dim3(512), 0, stream, prm);
-  e = hipGetLastError();
+  e = launch_kernel(attn_bwd_dq_kernel<D, CAUSAL>, dim3(grid), dim3(512), stream, prm);
   if (e != hipSuccess) return e;
   prm.n_ktiles = prm.n_tiles;
   if constexpr (D == 128) {
-    hipLaunchKernelGGL((attn_bwd_dkdv_pp_kernel<D, CAUSAL, 1, 64>), dim3(grid), dim3(512), 0, stream, prm);
-    e = hipGetLastError();
+    e = launch_kernel(attn_bwd_dkdv_pp_kernel<D, CAUSAL, 1, 64>, dim3(grid), dim3(512), stream, prm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, 2>), dim3(grid), dim3(512), 0, stream, prm);
+    return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, 2>, dim3(grid), dim3(512), stream, prm);
   } else {
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, CAUSAL, 3>), dim3(grid), dim3(512), 0, stream, prm);
+    return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, 3>, dim3(grid), dim3(512), stream, prm);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,

@@ -488,9 +488,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
 // ---------------------------------------------------------------------------
 template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_bf16_t(const FwdParams& prm, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((attn_fwd_bf16_kernel<D, NW, BC, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream,
-                     prm);
-  return hipGetLastError();
+  return launch_kernel(attn_fwd_bf16_kernel<D, NW, BC, CAUSAL>, dim3(grid), dim3(NW * 64), stream,
+                       prm);
 }
 
 // Waves per work-group: 8 (two per SIMD, one of each ping-pong group).

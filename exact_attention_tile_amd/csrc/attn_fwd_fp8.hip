@@ -506,16 +506,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
 
 template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_fp8_t(const FwdParams& prm, int grid, bool two_pass, hipStream_t stream) {
-  if (!two_pass) {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 0>), dim3(grid), dim3(NW * 64), 0,
+  if (!two_pass)
+    return launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 0>, dim3(grid), dim3(NW * 64),
+                         stream, prm);
+  const hipError_t e = launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 1>, dim3(grid),
+                                     dim3(NW * 64), stream, prm);
+  if (e != hipSuccess) return e;
+  return launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 2>, dim3(grid), dim3(NW * 64),
                        stream, prm);
-  } else {
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 1>), dim3(grid), dim3(NW * 64), 0,
-                       stream, prm);
-    hipLaunchKernelGGL((attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 2>), dim3(grid), dim3(NW * 64), 0,
-                       stream, prm);
-  }
-  return hipGetLastError();
 }
 
 // Waves per work-group: 8 (two per SIMD, one of each ping-pong group);

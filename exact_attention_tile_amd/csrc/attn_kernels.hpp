@@ -191,4 +191,17 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
+// Host side: enqueues `kernel` on `stream` and returns the status of that
+// launch alone (hipGetLastError would also report an earlier, unrelated
+// failure on the calling thread).  The arguments are taken by value with
+// the kernel's own parameter types.
+template <typename T> struct same_type { using type = T; };
+
+template <typename... KArgs>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                                hipStream_t stream, typename same_type<KArgs>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+}
+
 }  // namespace attn

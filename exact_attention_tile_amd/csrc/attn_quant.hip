@@ -258,20 +258,21 @@ hipError_t launch_quant(const void* x, void* codes, float* descale, const unsign
   const int nchunks = (N + kQuantRows - 1) / kQuantRows;
   QuantParams prm = {x, codes, descale, signs, N, H, nchunks};
   const dim3 grid((unsigned)(bh * nchunks));
-  if (d == 128)
-    hipLaunchKernelGGL((attn_quant_amax_kernel<128>), grid, dim3(kQuantThreads), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((attn_quant_amax_kernel<64>), grid, dim3(kQuantThreads), 0, stream, prm);
-  hipLaunchKernelGGL(attn_quant_reduce_kernel, dim3((bh + 3) / 4), dim3(256), 0, stream, prm, bh);
-  if (d == 128)
-    hipLaunchKernelGGL((attn_quant_codes_kernel<128>), grid, dim3(kQuantThreads), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((attn_quant_codes_kernel<64>), grid, dim3(kQuantThreads), 0, stream, prm);
+  // stop at the first launch that fails: the later kernels read what the
+  // earlier ones write
+  hipError_t e = d == 128
+      ? launch_kernel(attn_quant_amax_kernel<128>, grid, dim3(kQuantThreads), stream, prm)
+      : launch_kernel(attn_quant_amax_kernel<64>, grid, dim3(kQuantThreads), stream, prm);
+  if (e != hipSuccess) return e;
+  e = launch_kernel(attn_quant_reduce_kernel, dim3((bh + 3) / 4), dim3(256), stream, prm, bh);
+  if (e != hipSuccess) return e;
+  e = d == 128 ? launch_kernel(attn_quant_codes_kernel<128>, grid, dim3(kQuantThreads), stream, prm)
+               : launch_kernel(attn_quant_codes_kernel<64>, grid, dim3(kQuantThreads), stream, prm);
+  if (e != hipSuccess) return e;
   // 1/sqrt(d) rounded once to binary32 (exact for d = 64)
   const float post = signs ? (float)(1.0 / std::sqrt((double)d)) : 0.f;
   const int small = (bh + 255) / 256 < 1024 ? (bh + 255) / 256 : 1024;
-  hipLaunchKernelGGL(attn_quant_final_kernel, dim3(small), dim3(256), 0, stream, descale, bh, post);
-  return hipGetLastError();
+  return launch_kernel(attn_quant_final_kernel, dim3(small), dim3(256), stream, descale, bh, post);
 }
 
 }  // namespace attn
