@@ -428,13 +428,37 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       else
         phase_y(F_{}, 0, T_{});
       y_end();
-      int t = 1;
-      for (; t < t_plain; ++t) {        // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked
-        phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
+      // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked.  At d = 128 the loop
+      // is unrolled by two so that each step's buffers are compile-time
+      // constants, folded into the LDS reads' offsets (t is odd in the first
+      // step); that takes the address arithmetic out of the matrix-core
+      // phase.  At d = 64 the unrolled form measured slower.
+      auto plain_step = [&](auto odd_tag, int t) __attribute__((always_inline)) {
+        constexpr bool ODD = decltype(odd_tag)::value;
+        phase_x(T_{}, T_{}, ks_base + (ODD ? TILE : 0), vs_base + (ODD ? 0 : TILE));
         x_end();
         y_start();
         phase_y(F_{}, t * BC, F_{});
         y_end();
+      };
+      int t = 1;
+      if constexpr (D == 128) {
+        for (; t + 1 < t_plain; t += 2) {
+          plain_step(T_{}, t);
+          plain_step(F_{}, t + 1);
+        }
+        if (t < t_plain) {
+          plain_step(T_{}, t);
+          ++t;
+        }
+      } else {
+        for (; t < t_plain; ++t) {
+          phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
+          x_end();
+          y_start();
+          phase_y(F_{}, t * BC, F_{});
+          y_end();
+        }
       }
       for (; t < T; ++t) {              // the masked tail
         phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
