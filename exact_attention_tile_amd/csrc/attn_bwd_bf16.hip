@@ -349,10 +349,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   __syncthreads();
 
   // one K/V tile of this wave: S^T and dP^T, dS^T, dQ^T += K^T dS^T
-  auto tile = [&](auto masked_tag, int j) __attribute__((always_inline)) {
+  // buf_tag: the buffer of tile j (j & 1) when known at compile time
+  // (0 or 1: the LDS addresses fold into the reads' offsets), else -1
+  auto tile = [&](auto masked_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const __bf16* kt = ks_base + (j & 1) * TILE;
-    const __bf16* vt = vs_base + (j & 1) * TILE;
+    constexpr int BUF = decltype(buf_tag)::value;
+    const int buf = BUF < 0 ? (j & 1) : BUF;
+    const __bf16* kt = ks_base + buf * TILE;
+    const __bf16* vt = vs_base + buf * TILE;
     const int kv0 = j * BC;
     f32x16 s[NKB], dp[NKB];
     // the matrix-core sections raise the wave's issue priority, so that
@@ -421,15 +425,27 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   if (CAUSAL) first_masked = min(first_masked, (qw0 + 1) / BC);
   using T_ = std::true_type;
   using F_ = std::false_type;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using BRT = std::integral_constant<int, -1>;
   int j = 0;
-  for (const int j_plain = min(first_masked, wv_tiles); j < j_plain; ++j) {
+  const int j_plain = min(first_masked, wv_tiles);
+  for (; j + 1 < j_plain; j += 2) {     // unmasked, two tiles per step (j even)
     next_loads(j);
-    tile(F_{}, j);
+    tile(F_{}, B0{}, j);
+    end_tile();
+    next_loads(j + 1);
+    tile(F_{}, B1{}, j + 1);
+    end_tile();
+  }
+  for (; j < j_plain; ++j) {
+    next_loads(j);
+    tile(F_{}, BRT{}, j);
     end_tile();
   }
   for (; j < wv_tiles; ++j) {
     next_loads(j);
-    tile(T_{}, j);
+    tile(T_{}, BRT{}, j);
     end_tile();
   }
   for (; j < wg_tiles; ++j) {           // the other waves' tiles: loads and barriers only
@@ -554,9 +570,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __syncthreads();
 
   // one query tile j of this wave's keys
-  auto tile = [&](auto masked_tag, int j) __attribute__((always_inline)) {
+  // buf_tag: the buffer of tile j ((j - first) & 1) when known at compile
+  // time (0 or 1: the LDS addresses fold into the reads' offsets), else -1
+  auto tile = [&](auto masked_tag, auto buf_tag, int j) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    const int buf = (j - first) & 1;
+    constexpr int BUF = decltype(buf_tag)::value;
+    const int buf = BUF < 0 ? ((j - first) & 1) : BUF;
     const int qt0 = j * BQ;
     const __bf16* qt = qs_base + buf * TILE;
     const __bf16* gt = gs_base + buf * TILE;
@@ -647,6 +666,9 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   const int seg_c = max(seg_b, min(N / BQ, n));
   using T_ = std::true_type;
   using F_ = std::false_type;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using BRT = std::integral_constant<int, -1>;
   int j = first;
   for (; j < min(j_act, n); ++j) {      // inactive: loads and barriers only
     next_loads(j);
@@ -654,17 +676,33 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   }
   for (; j < seg_b; ++j) {
     next_loads(j);
-    tile(T_{}, j);
+    tile(T_{}, BRT{}, j);
     end_tile(j);
+  }
+  // unmasked: two tiles per step from an even (j - first), so that the
+  // buffers of each step are known at compile time
+  if (j < seg_c && ((j - first) & 1)) {
+    next_loads(j);
+    tile(F_{}, BRT{}, j);
+    end_tile(j);
+    ++j;
+  }
+  for (; j + 1 < seg_c; j += 2) {
+    next_loads(j);
+    tile(F_{}, B0{}, j);
+    end_tile(j);
+    next_loads(j + 1);
+    tile(F_{}, B1{}, j + 1);
+    end_tile(j + 1);
   }
   for (; j < seg_c; ++j) {
     next_loads(j);
-    tile(F_{}, j);
+    tile(F_{}, BRT{}, j);
     end_tile(j);
   }
   for (; j < n; ++j) {
     next_loads(j);
-    tile(T_{}, j);
+    tile(T_{}, BRT{}, j);
     end_tile(j);
   }
 
