@@ -1,6 +1,6 @@
 """Throughput of the tiled exact attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload long8k]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload ctx32k]
                     [--no-cpu-baseline] [--copy-calibration]
 
 A step is one pass of the whole hot path -- one attn_fwd (or attn_fwd_fp8)
@@ -10,10 +10,11 @@ seeded synthetic inputs already resident in HBM.  W untimed steps, then K
 steps timed with HIP events on the stream the kernel is launched on (torch's
 current stream).  Prints ONE JSON line.
 
-Default workload long8k: B=2, H=16, N=8192, d=128, bf16, causal, scale
-1/sqrt(d) -- the first bf16 workload at the N >= 8192, d = 128 size the
-throughput target is stated for.  Other workloads (--workload) are for
-exploration; the parity tests cover all of them.
+Default workload ctx32k: B=1, H=32, N=32768, d=128, bf16, causal, scale
+1/sqrt(d), 1% of each head's K rows scaled by 8 -- the largest configuration
+the throughput target is stated for (N >= 8192, d = 128) that fits one GPU.
+Other workloads (--workload: long8k, fp8_8k, ...) are timed the same way;
+the parity tests cover all of them.
 
 TFLOPS = 4*B*H*N^2*d (halved when causal) / time per step.
 
@@ -49,11 +50,17 @@ PEAK_HBM_GBS = 8000.0
 METRIC_FWD2 = ("attn fwd fp8 two-pass TFLOPS (4BHN²d, causal halved; the row-maximum pass is "
                "not counted) + % of MI355X MFMA peak, 1 GPU")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.txt")
+MICROBENCH_FILE = os.path.join(ROOT, "profiles", "gfx950_microbench.md")
+CUS, SIMDS, XCDS, CLOCK_GHZ = 256, 1024, 8, 2.4
+SQ_FIELDS = ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+             "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "GRBM_GUI_ACTIVE"]
 
 
 KERNEL_SOURCES = {"quant": ("attn_quant.hip", "attn_kernels.hpp", "attn_api.cpp"),
                   "bf16": ("attn_fwd_bf16.hip", "attn_kernels.hpp", "attn_api.cpp"),
-                  "fp8": ("attn_fwd_fp8.hip", "attn_kernels.hpp", "attn_api.cpp")}
+                  "fp8": ("attn_fwd_fp8.hip", "attn_kernels.hpp", "attn_api.cpp"),
+                  "bwd": ("attn_bwd_bf16.hip", "attn_kernels.hpp", "attn_api.cpp")}
 
 
 def kernel_source_hash(dtype):
@@ -85,6 +92,106 @@ def measured_traffic(workload, dtype, causal, key=None):
     except (OSError, ValueError):
         return None
     return None
+
+
+def measured_counters(key, dtype):
+    """Figures derived from the committed SQ counter run of the kernel
+    (profiles/counters.txt, per-launch averages), if it was taken on the
+    current kernel sources; else None:
+      mfma_busy      SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x engine cycles
+                     per XCD): the fraction of the launch the matrix cores
+                     were busy, at the clock the chip held;
+      valu_per_mfma  SQ_INSTS_VALU / SQ_INSTS_MFMA;
+      lds_per_mfma   SQ_INSTS_LDS / SQ_INSTS_MFMA;
+      clock_mhz      GRBM_GUI_ACTIVE / 8 XCDs / the launch's duration under
+                     counters (the engine clock held over the launch);
+      lds_bank_conflict_cycles."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            for line in f:
+                fields = line.split()
+                if len(fields) == 2 + len(SQ_FIELDS) + 1 and fields[0] == key:
+                    if fields[1] != kernel_source_hash(dtype):
+                        return None
+                    v = dict(zip(SQ_FIELDS, map(float, fields[2:2 + len(SQ_FIELDS)])))
+                    dur_ns = float(fields[-1])
+                    cycles = v["GRBM_GUI_ACTIVE"] / XCDS
+                    return {
+                        "source": "profiles/counters.txt (rocprofv3 --pmc, key %s)" % key,
+                        "mfma_busy": round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles), 4),
+                        "valu_per_mfma": round(v["SQ_INSTS_VALU"] / v["SQ_INSTS_MFMA"], 3),
+                        "lds_per_mfma": round(v["SQ_INSTS_LDS"] / v["SQ_INSTS_MFMA"], 3),
+                        "clock_mhz": round(cycles / dur_ns * 1e3, 1),
+                        "lds_bank_conflict_cycles": v["SQ_LDS_BANK_CONFLICT"],
+                        "sq_insts_valu": v["SQ_INSTS_VALU"],
+                    }
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def microbench_figures():
+    """From the committed microbenchmark table (profiles/gfx950_microbench.md):
+    cycles per v_fma_f32 per SIMD with one wave per SIMD, and LDS bytes read
+    per cycle per compute unit by ds_read_b128 and ds_read_b64_tr_b16 with
+    16 waves.  None where the table is missing."""
+    out = {"valu_cycles": None, "lds_b128": None, "lds_tr16": None}
+    try:
+        with open(MICROBENCH_FILE) as f:
+            for line in f:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                if len(cells) < 4:
+                    continue
+                try:
+                    num = float(cells[3].split()[0])
+                except (ValueError, IndexError):
+                    continue
+                if cells[0] == "valu" and cells[1] == "v_fma_f32" and cells[2].startswith("1 "):
+                    out["valu_cycles"] = num
+                elif cells[0] == "lds" and cells[2].startswith("16 "):
+                    if cells[1] == "ds_read_b128":
+                        out["lds_b128"] = num
+                    elif cells[1] == "ds_read_b64_tr_b16":
+                        out["lds_tr16"] = num
+    except OSError:
+        pass
+    return out
+
+
+def algorithmic_bytes(w):
+    """HBM bytes one forward launch must move: Q, K, V read once, O and LSE
+    written once."""
+    e = 1 if w.dtype == "fp8" else 2
+    T = w.total
+    return T * w.d * (w.H * e + 2 * w.kv_heads * e + w.H * 2) + T * w.H * 4
+
+
+def secondary_roofs(w, flops, achieved, ctr, mb):
+    """The two on-chip roofs beside the matrix-core peak, in TFLOP/s of the
+    metric's flops (each at the nominal 2.4 GHz, like the peak):
+      valu  the launch's vector ALU instructions (SQ_INSTS_VALU) issued back
+            to back at the measured cycles per instruction, spread over the
+            1024 SIMDs;
+      lds   the K and V operand reads from LDS: each 32-query wave reads the
+            whole K and V tile for every tile it visits, 2 * d * e bytes per
+            key, i.e. e / 64 bytes per flop (e = 2 bf16, 1 fp8), against the
+            measured ds_read bandwidth (ds_read_b128 for K, the transposing
+            read for V: their mean)."""
+    out = {}
+    if ctr is not None and mb["valu_cycles"]:
+        t = ctr["sq_insts_valu"] / SIMDS * mb["valu_cycles"] / (CLOCK_GHZ * 1e9)
+        roof = flops / t / 1e12
+        out["valu"] = {"roof": round(roof, 1), "frac": round(achieved / roof, 4),
+                       "basis": "SQ_INSTS_VALU x %.2f cycles / 1024 SIMDs at 2.4 GHz"
+                                % mb["valu_cycles"]}
+    if mb["lds_b128"] and mb["lds_tr16"]:
+        e = 1 if w.dtype == "fp8" else 2
+        bw = 0.5 * (mb["lds_b128"] + mb["lds_tr16"]) * CUS * CLOCK_GHZ * 1e9
+        roof = bw / (e / 64.0) / 1e12
+        out["lds"] = {"roof": round(roof, 1), "frac": round(achieved / roof, 4),
+                      "basis": "%.3f LDS bytes per flop at %.1f B/clk/CU" % (
+                          e / 64.0, 0.5 * (mb["lds_b128"] + mb["lds_tr16"]))}
+    return out or None
 
 
 def _head_problem(w, inp, b, h):
@@ -160,14 +267,18 @@ def cpu_baseline(w, inp, causal, budget_s=12.0):
         if dt >= 0.5 * budget_s or count >= max(lens) or attempt == 2:
             break
         count = int(min(max(lens), count * budget_s / max(dt, 1e-3)))
+    rate = flops / dt
     return {
-        "value": flops / dt / 1e12,
+        "value": rate / 1e12,
         "unit": "TFLOPS",
         "cores": int(cores),
         "kind": "oracle",
         "sample": "fp64 NumPy oracle on up to %d seeded query rows of each of %d/%d (batch, head) "
                   "problems (%d rows, %.2f GFLOP counted with the metric's 4*d*visible_keys per "
                   "row, %.1f s)" % (count, done, len(heads), nrows, flops / 1e9, dt),
+        "extrapolated_full_config_s": round(w.flops(causal) / rate, 1),
+        "extrapolation": "an extrapolation, not a measurement: the whole workload's flops "
+                         "(%.4g) at the sample's rate" % w.flops(causal),
     }
 
 
@@ -254,7 +365,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="long8k")
+    ap.add_argument("--workload", default="ctx32k")
     ap.add_argument("--causal", type=int, default=None, help="override the workload's mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pass", dest="which", choices=["fwd", "fwd2", "bwd", "quant"], default="fwd",
@@ -445,9 +556,20 @@ def main():
                      "kernel_median_ms": round(statistics.median(launch_ms), 4),
                      "kernel_min_ms": round(min(launch_ms), 4)},
     }
+    rf = out["roofline"]
+    if args.which == "fwd":
+        rf["algorithmic_bytes"] = algorithmic_bytes(w)
+        rf["traffic_ratio"] = (round(rf["traffic"] / rf["algorithmic_bytes"], 3)
+                               if rf["traffic"] else None)
+        key = "%s_%s" % (w.name, "causal" if causal else "noncausal")
+        ctr = measured_counters(key, w.dtype)
+        rf["counters"] = ctr
+        rf["secondary"] = secondary_roofs(w, flops, achieved, ctr, microbench_figures())
+        if ctr is not None:
+            del ctr["sq_insts_valu"]
     if args.which in ("bwd", "fwd2"):
         out["config"]["pass"] = args.which
-        out["roofline"]["traffic"] = None
+        rf["traffic"] = None
     if args.which == "fwd2":
         out["metric"] = METRIC_FWD2
     if not args.no_cpu_baseline and args.which in ("fwd", "fwd2"):

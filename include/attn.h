@@ -36,11 +36,17 @@
  *   - Any N >= 1 is accepted; ragged tails are masked, never truncated.
  *   - Pointers are DEVICE pointers owned by the caller, who keeps them alive
  *     until the work queued on `stream` has completed.  The library
- *     allocates nothing, frees nothing and never synchronises; each call
- *     only enqueues one kernel on `stream` (0 = the null stream).
- *   - Errors are detected on the host before any HIP call; nothing is
- *     launched when a call returns an error.  The functions are stateless
- *     and thread-safe.
+ *     allocates nothing, frees nothing and never synchronises.  The
+ *     single-pass forwards (attn_fwd, attn_fwd_fp8 and their grouped-query
+ *     and variable-length forms) enqueue exactly one kernel on `stream`
+ *     (0 = the null stream); attn_fwd_fp8_2pass enqueues two, attn_bwd three
+ *     or four and attn_fp8_quantize four, in order on the same stream.
+ *   - Argument errors (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED) are
+ *     detected on the host before any HIP call; nothing is launched then.
+ *     ATTN_ERR_HIP reports a failed launch: for a multi-kernel entry point
+ *     the kernels enqueued before the failing one stay enqueued and may have
+ *     written part of the outputs (or the workspace), which are then
+ *     unspecified.  The functions are stateless and thread-safe.
  *   - Inputs must be finite; results for inf/NaN inputs are unspecified.
  *   - o must not alias q, k or v.
  */

@@ -1,0 +1,185 @@
+"""Runs the gfx950 microbenchmarks of ``mb_kernels.hip`` on cuda:0 and
+prints a Markdown table (also written to ``--out``).
+
+    python -m microbench.run [--out FILE] [--quick]
+
+Every figure is in cycles of the shader clock (s_memtime), taken per wave
+around the timed loop; one work-group per compute unit.  The clock each run
+held is the shader cycles over the real-time counter (100 MHz).
+
+Rows:
+  valu      cycles per vector instruction per SIMD, for 16 independent chains
+            of one operation (fma, exp, add, cvt_pk_bf16) or a softmax mix,
+            with 1, 2 or 4 waves per SIMD;
+  mfma      cycles per v_mfma_f32_32x32x16_bf16 per SIMD (4 independent
+            accumulators), accumulators in VGPRs or AGPRs, alone and with a
+            softmax-mix wave on the same SIMD (and that wave's cycles per
+            vector instruction);
+  lds       LDS bytes read per cycle per compute unit (ds_read_b128,
+            ds_read_b64, ds_read_b64_tr_b16) with 4, 8 or 16 waves;
+  mfma+lds  cycles per MFMA when its A operand is a 1 KiB ds_read_b128
+            fragment, as in the attention kernels' matrix-core phase.
+"""
+
+import argparse
+import os
+import statistics
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def _stamps(buf, waves):
+    a = buf.cpu().numpy().reshape(-1, waves, 4).astype(np.float64)
+    return a   # [grid][waves][c0, c1, r0, r1]
+
+
+class Runner:
+    def __init__(self, grid):
+        import torch
+        import microbench
+        self.torch = torch
+        self.lib = microbench.load()
+        self.grid = grid
+        self.stream = torch.cuda.current_stream().cuda_stream
+        self.stamps = torch.zeros(grid * 16 * 4, dtype=torch.int64, device="cuda")
+        self.sink = torch.zeros(grid * 1024, dtype=torch.float32, device="cuda")
+
+    def _launch(self, fn, *args):
+        for _ in range(2):                       # the first launch warms up
+            st = fn(*args, self.stamps.data_ptr(), self.sink.data_ptr(), self.stream)
+            if st != 0:
+                raise RuntimeError("launch failed: hipError %d" % st)
+        self.torch.cuda.synchronize()
+
+    def valu(self, op, waves, iters):
+        self._launch(self.lib.mb_valu_rate, op, self.grid, waves, iters)
+        s = _stamps(self.stamps[:self.grid * waves * 4], waves)
+        cyc = s[:, :, 1] - s[:, :, 0]
+        rt = s[:, :, 3] - s[:, :, 2]
+        return cyc, rt
+
+    def pair(self, acc, mfma_waves, valu, iters):
+        self._launch(self.lib.mb_mfma_pair, acc, self.grid, mfma_waves, valu, iters)
+        s = _stamps(self.stamps[:self.grid * 8 * 4], 8)
+        return s[:, :, 1] - s[:, :, 0], s[:, :, 3] - s[:, :, 2]
+
+    def lds(self, kind, waves, iters):
+        self._launch(self.lib.mb_lds_read, kind, self.grid, waves, iters)
+        s = _stamps(self.stamps[:self.grid * waves * 4], waves)
+        return s[:, :, 1] - s[:, :, 0], s[:, :, 3] - s[:, :, 2]
+
+    def mfma_lds(self, mfma_waves, valu, iters):
+        self._launch(self.lib.mb_mfma_lds, self.grid, mfma_waves, valu, iters)
+        s = _stamps(self.stamps[:self.grid * 8 * 4], 8)
+        return s[:, :, 1] - s[:, :, 0], s[:, :, 3] - s[:, :, 2]
+
+
+def _mhz(cyc, rt):
+    ok = rt > 0
+    return float(np.median(cyc[ok] / (rt[ok] * 10e-9) / 1e6)) if ok.any() else float("nan")
+
+
+VALU_OPS = [(0, "v_fma_f32", 16), (1, "v_exp_f32", 16), (2, "v_add_f32", 16),
+            (3, "v_cvt_pk_bf16_f32", 8), (4, "softmax mix (fma, exp, add, cvt, xor)", 57)]
+
+
+def run(quick=False):
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    grid = props.multi_processor_count
+    r = Runner(grid)
+    k = 4 if quick else 1
+    rows = []
+
+    # vector ALU issue rates
+    for op, name, per in VALU_OPS:
+        for waves in (4, 8, 16):
+            iters = 20000 // k
+            cyc, rt = r.valu(op, waves, iters)
+            per_simd = waves // 4
+            # the slowest wave of each work-group bounds its SIMDs
+            v = np.median(cyc.max(axis=1)) / (iters * per * per_simd)
+            rows.append(("valu", name, "%d wave(s)/SIMD" % per_simd,
+                         "%.2f cycles per instruction per SIMD" % v, _mhz(cyc, rt)))
+
+    # MFMA rate, alone and beside a vector wave
+    for acc, accname in ((0, "VGPR acc"), (1, "AGPR acc")):
+        iters = 4000 // k
+        cyc, rt = r.pair(acc, 4, 0, iters)
+        mf_alone = np.median(cyc[:, :4]) / (iters * 32)
+        rows.append(("mfma", "32x32x16 bf16, " + accname, "1 MFMA wave/SIMD",
+                     "%.2f cycles per MFMA" % mf_alone, _mhz(cyc[:, :4], rt[:, :4])))
+        cyc, rt = r.pair(acc, 8, 0, iters)
+        mf2 = np.median(cyc.max(axis=1)) / (iters * 32 * 2)
+        rows.append(("mfma", "32x32x16 bf16, " + accname, "2 MFMA waves/SIMD",
+                     "%.2f cycles per MFMA per SIMD" % mf2, _mhz(cyc, rt)))
+        cyc, rt = r.pair(acc, 4, 1, iters)
+        mf = np.median(cyc[:, :4]) / (iters * 32)
+        va = np.median(cyc[:, 4:]) / (4 * iters * 57)
+        rows.append(("mfma", "32x32x16 bf16, " + accname, "+1 softmax wave/SIMD",
+                     "%.2f cycles per MFMA; partner %.2f cycles per vector instruction "
+                     "(228 per 32 MFMAs)" % (mf, va), _mhz(cyc, rt)))
+    cyc, rt = r.pair(0, 0, 1, 4000 // k)
+    va = np.median(cyc[:, 4:]) / (4 * (4000 // k) * 57)
+    rows.append(("mfma", "(softmax wave alone)", "1 wave/SIMD",
+                 "%.2f cycles per vector instruction" % va, _mhz(cyc[:, 4:], rt[:, 4:])))
+
+    # LDS read bandwidth
+    for kind, name, nbytes in ((0, "ds_read_b128", 1024), (1, "ds_read_b64", 512),
+                               (2, "ds_read_b64_tr_b16", 512)):
+        for waves in (4, 8, 16):
+            iters = 8000 // k
+            cyc, rt = r.lds(kind, waves, iters)
+            bpc = waves * iters * 8 * nbytes / cyc.max(axis=1)
+            rows.append(("lds", name, "%d waves/CU" % waves,
+                         "%.1f bytes per cycle per CU" % float(np.median(bpc)), _mhz(cyc, rt)))
+
+    # MFMA with its A operand from LDS
+    iters = 8000 // k
+    for mw, valu, label in ((4, 0, "1 MFMA wave/SIMD"), (8, 0, "2 MFMA waves/SIMD"),
+                            (4, 1, "1 MFMA wave + 1 softmax wave/SIMD")):
+        cyc, rt = r.mfma_lds(mw, valu, iters)
+        per_simd = mw // 4
+        mf = np.median(cyc[:, :mw].max(axis=1)) / (iters * 16 * per_simd)
+        txt = "%.2f cycles per MFMA per SIMD (%.1f LDS bytes per cycle per CU)" % (
+            mf, 4 * 1024 / mf)
+        if valu:
+            va = np.median(cyc[:, 4:]) / (2 * iters * 57)
+            txt += "; partner %.2f cycles per vector instruction" % va
+        rows.append(("mfma+lds", "32x32x16 bf16, A from ds_read_b128", label, txt,
+                     _mhz(cyc, rt)))
+    return props, rows
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=None)
+    ap.add_argument("--quick", action="store_true", help="a quarter of the iterations")
+    args = ap.parse_args()
+    import torch
+    if not torch.cuda.is_available():
+        print("microbench needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    props, rows = run(args.quick)
+    lines = ["# gfx950 microbenchmarks", "",
+             "Command: `python -m microbench.run%s`" % (" --quick" if args.quick else ""), "",
+             "Device: %s, %d compute units; one work-group per compute unit; figures in shader "
+             "clock cycles (s_memtime), median over work-groups." % (props.name,
+                                                                   props.multi_processor_count),
+             "", "| unit | what | waves | result | clock MHz |", "|---|---|---|---|---|"]
+    for row in rows:
+        lines.append("| %s | %s | %s | %s | %.0f |" % row)
+    text = "\n".join(lines) + "\n"
+    print(text, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,8 +19,8 @@ import torch
 import exact_attention_tile_amd as eat
 from oracle import (attention_forward_gqa, attention_forward_varlen, bf16_bits_to_float64,
                     dequantize_e4m3)
-from parity_common import (LSE_MAXABS, FP8_LSE_ACC, SENTINEL_BF16, SENTINEL_F32, Guarded,
-                           assert_bf16_ok, assert_fp8_ok, dev_u16, dev_u8, errors, require_gpu)
+from parity_common import (SENTINEL_BF16, SENTINEL_F32, Guarded, assert_bf16_ok, assert_fp8_ok,
+                           dev_u16, dev_u8, error_figures, errors, lse_bound_rows, require_gpu)
 from workloads import WORKLOADS, Workload, make_inputs, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -60,16 +60,6 @@ def _decode(inp, dtype, cu=None):
     return tuple(out)
 
 
-def _lse_bound(q, k, scale, causal, rows):
-    """fp8 LSE tolerance 1e-3 + 2^-10 * A_i (parity_common) for one head:
-    q [n][d], k [n][d] float64, rows: the query rows checked."""
-    rows = np.asarray(rows)
-    a = abs(scale) * (np.abs(q[rows]) @ np.abs(k).T)
-    if causal:
-        a = np.where(np.arange(k.shape[0])[None, :] <= rows[:, None], a, 0.0)
-    return LSE_MAXABS + FP8_LSE_ACC * a.max(axis=1)
-
-
 # ---------------------------------------------------------------------------
 # grouped-query
 # ---------------------------------------------------------------------------
@@ -103,7 +93,7 @@ def _check_gqa(w, inp, out, causal, rows=None):
         for b in range(w.B):
             for h in range(w.H):
                 r = np.arange(w.N) if rows is None else rows[b, h]
-                bound[b, h] = _lse_bound(q[b, :, h], k[b, :, h // g], w.scale, causal, r)
+                bound[b, h] = lse_bound_rows(q[b, :, h], k[b, :, h // g], w.scale, causal, r)
         assert_fp8_ok(errors(out, ro, rl, rows, lse_bound=bound), label)
     else:
         assert_bf16_ok(errors(out, ro, rl, rows), label)
@@ -187,19 +177,15 @@ def _check_varlen(w, inp, out, causal, rows, skip=()):
             gl.append(lse[h, s0 + r[h]])
             grl.append(rl[b][h])
             if w.dtype == "fp8":
-                bnd.append(_lse_bound(q[0, s0:cu[b + 1], h], k[0, s0:cu[b + 1], h // g], w.scale,
+                bnd.append(lse_bound_rows(q[0, s0:cu[b + 1], h], k[0, s0:cu[b + 1], h // g], w.scale,
                                       causal, r[h]))
     go, gr = np.concatenate(go), np.concatenate(gr)
     gl, grl = np.concatenate(gl), np.concatenate(grl)
-    diff = go - gr
-    max_abs = float(np.abs(diff).max())
-    rel_rms = float(np.sqrt((diff ** 2).sum() / (gr ** 2).sum()))
     label = "%s causal=%d" % (w.name, causal)
     if w.dtype == "fp8":
-        assert_fp8_ok((max_abs, rel_rms, float((np.abs(gl - grl) / np.concatenate(bnd)).max())),
-                      label)
+        assert_fp8_ok(error_figures(go, gr, gl, grl, np.concatenate(bnd)), label)
     else:
-        assert_bf16_ok((max_abs, rel_rms, float(np.abs(gl - grl).max())), label)
+        assert_bf16_ok(error_figures(go, gr, gl, grl), label)
 
 
 VARLEN_EDGE = [("bf16", (300, 1, 0, 129, 64), 4, 2, 64), ("bf16", (1000, 17, 256, 1), 6, 3, 128),

@@ -1,9 +1,19 @@
-"""Work order and mask segments of the attention kernels, restated here.
+"""Work order and mask segments of the attention kernels, as a Python model.
 
-Block order: the fixed-length forward kernels (attn_kernels.hpp,
-block_to_work, with the order the host's plan() picks in attn_api.cpp) must
-map every launch index to a distinct (batch*head, query tile) pair, so that
-each query tile is computed exactly once.
+These tests check a Python restatement of the device and host logic, not the
+compiled code: plan_remap / block_order below re-implement plan()
+(attn_api.cpp) and block_to_work (attn_kernels.hpp), and the segment bounds
+re-implement the kernels' loop limits.  They pin the design -- that the
+chosen orders are bijections and that the segment bounds agree with the
+per-tile mask definition -- so a change to the model that breaks it fails
+here.  Whether the compiled kernels follow the model is checked on the GPU:
+every parity test covers each query tile's rows (sampled or whole) and the
+guard bands around O and LSE, so a launch index mapped twice or never shows
+there as a wrong or missing row.
+
+Block order: the fixed-length forward kernels must map every launch index to
+a distinct (batch*head, query tile) pair, so that each query tile is
+computed exactly once.
 
 Mask segments: the forward, dQ and dK/dV tile loops run the tiles that need
 no mask through a body without it; the segment bounds must agree with the
