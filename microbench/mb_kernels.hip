@@ -39,32 +39,54 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #define MB_LDS __attribute__((address_space(3)))
 
 // Per-wave record: shader clock at start and end, real-time clock at start
-// and end (4 x uint64).  Written by lane 0 of each wave with a vector store.
+// and end, the wave's HW_ID register (SIMD, CU, shader array and engine
+// fields) and XCC_ID (8 x uint64).  Written by lane 0 of each wave with a
+// vector store.
 struct Stamp {
-  unsigned long long c0, c1, r0, r1;
+  unsigned long long c0, c1, r0, r1, hw_id, xcc_id, pad0, pad1;
 };
 
 __device__ __forceinline__ void stamp_store(Stamp* out, int waves, unsigned long long c0,
                                             unsigned long long c1, unsigned long long r0,
                                             unsigned long long r1) {
   const int wave = threadIdx.x >> 6;
+  unsigned hw, xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   if ((threadIdx.x & 63) == 0) {
-    Stamp s = {c0, c1, r0, r1};
+    Stamp s = {c0, c1, r0, r1, hw, xcc, 0, 0};
     out[blockIdx.x * waves + wave] = s;
   }
 }
+
+// Occupancy guard: a timed kernel reserves PAD bytes of LDS (more than half
+// of the 160 KiB of a compute unit) so that no two of its work-groups share
+// a compute unit.  The array is touched only on a path no launch takes
+// (iters < 0 is rejected by the host entry points), which keeps it
+// allocated.
+constexpr int PAD = 96 * 1024;
+#define MB_RESERVE_LDS(iters)                                             \
+  __shared__ unsigned char mb_pad[PAD];                                   \
+  if ((iters) < 0) {                                                      \
+    mb_pad[threadIdx.x] = (unsigned char)threadIdx.x;                     \
+    __syncthreads();                                                      \
+    sink[threadIdx.x] = (float)mb_pad[(threadIdx.x + 1) % blockDim.x];    \
+    return;                                                               \
+  }
 
 // ---------------------------------------------------------------------------
 // 1. vector ALU issue rate: 16 independent chains of one operation
 // ---------------------------------------------------------------------------
 // OP 0 v_fma_f32, 1 v_exp_f32, 2 v_add_f32, 3 v_cvt_pk_bf16_f32,
+//    5 v_exp_f32 and v_fma_f32 alternating on independent chains (8 + 8),
 //    4 a softmax mix: per pair of scores 2 fma, 2 exp, 2 add, 1 cvt_pk and
 //      1 xor (which keeps the conversion live), 7 pairs per iteration.
-// Vector instructions per iteration: 16 (OP 0-2), 8 (OP 3), 57 (OP 4: the
-// 7 x 8 above and one multiply).
+// Vector instructions per iteration: 16 (OP 0-2, 5), 8 (OP 3), 57 (OP 4:
+// the 7 x 8 above and one multiply).
 template <int OP>
 __global__ __launch_bounds__(1024, 1) void valu_rate(Stamp* out, float* sink, int iters,
                                                      float seed) {
+  MB_RESERVE_LDS(iters);
   float x[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) x[i] = seed * (float)(threadIdx.x + 3 * i + 1);
@@ -84,6 +106,14 @@ __global__ __launch_bounds__(1024, 1) void valu_rate(Stamp* out, float* sink, in
     } else if constexpr (OP == 2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) x[i] = x[i] + a;
+    } else if constexpr (OP == 5) {
+      // 8 exponential chains and 8 fma chains, independent of each other:
+      // does the transcendental unit run beside the fma path?
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[i] = __builtin_amdgcn_exp2f(-x[i]);
+        x[i + 8] = __builtin_fmaf(x[i + 8], a, bconst);
+      }
     } else if constexpr (OP == 3) {
 #pragma unroll
       for (int i = 0; i < 16; i += 2) {
@@ -122,15 +152,16 @@ __global__ __launch_bounds__(1024, 1) void valu_rate(Stamp* out, float* sink, in
 // 2. MFMA rate, and MFMA beside a vector wave on the same SIMD
 // ---------------------------------------------------------------------------
 // Waves w < mfma_waves issue v_mfma_f32_32x32x16_bf16 on 4 independent
-// accumulators (32 MFMAs per iteration); with `valu` set, the other waves
-// run the softmax mix of valu_rate<4> (57 vector instructions per mix
-// iteration, 4 mix iterations per MFMA iteration: 228 per 32 MFMAs, about
-// the 7 per pair of scores of 64 keys x 32 queries).  ACC 0: the
+// accumulators (32 MFMAs per iteration); with `valu` set, waves 4-7 (those
+// not issuing MFMAs) run the softmax mix of valu_rate<4> (57 vector
+// instructions per mix iteration, 2 mix iterations per MFMA iteration: 114
+// per 32 MFMAs, the attention kernels' ratio for 64 keys x 32 queries).  ACC 0: the
 // accumulators in VGPRs (compiler builtin), ACC 1: in AGPRs (asm).
 // Waves i and i + 4 of a work-group share a SIMD.
 template <int ACC>
 __global__ __launch_bounds__(512, 1) void mfma_pair(Stamp* out, float* sink, int iters,
                                                     int mfma_waves, int valu, float seed) {
+  MB_RESERVE_LDS(iters);
   const int wave = threadIdx.x >> 6;
   float r = 0.f;
   __syncthreads();
@@ -167,7 +198,7 @@ __global__ __launch_bounds__(512, 1) void mfma_pair(Stamp* out, float* sink, int
       asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
     }
     r = acc0[0] + acc1[1] + acc2[2] + acc3[3];
-  } else if (valu) {
+  } else if (valu && wave >= 4) {
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = seed * (float)(threadIdx.x + i);
@@ -176,7 +207,7 @@ __global__ __launch_bounds__(512, 1) void mfma_pair(Stamp* out, float* sink, int
     const float cc = seed * 0.5f;
     c0 = __builtin_amdgcn_s_memtime();
     r0 = __builtin_amdgcn_s_memrealtime();
-    for (int it = 0; it < 4 * iters; ++it) {
+    for (int it = 0; it < 2 * iters; ++it) {
       const float m = l0 * 1e-30f;
 #pragma unroll
       for (int i = 0; i < 14; i += 2) {
@@ -214,10 +245,12 @@ __global__ __launch_bounds__(512, 1) void mfma_pair(Stamp* out, float* sink, int
 #define MB_R64(op, j) #op " %" #j ", %8 offset:" #j "*512\n\t"
 template <int KIND>
 __global__ __launch_bounds__(1024, 1) void lds_read(Stamp* out, float* sink, int iters) {
+  // 96 KiB, of which the reads cover the first 64: one work-group per CU
   constexpr int BYTES = 65536;
+  constexpr int ALLOC = 96 * 1024;
   constexpr int STEP = KIND == 0 ? 1024 : 512;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[BYTES];
-  for (int i = threadIdx.x * 16; i < BYTES; i += blockDim.x * 16)
+  __shared__ __attribute__((aligned(16))) unsigned char lds[ALLOC];
+  for (int i = threadIdx.x * 16; i < ALLOC; i += blockDim.x * 16)
     *(u32x4*)(lds + i) = u32x4{(unsigned)i, (unsigned)i + 1, (unsigned)i + 2, (unsigned)i + 3};
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -285,7 +318,8 @@ __global__ __launch_bounds__(1024, 1) void lds_read(Stamp* out, float* sink, int
 __global__ __launch_bounds__(512, 1) void mfma_lds(Stamp* out, float* sink, int iters,
                                                    int mfma_waves, int valu, float seed) {
   constexpr int D = 128;
-  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * D * 2];   // 32 KiB
+  // 32 KiB of K tiles, allocated as 96 KiB so that one work-group holds a CU
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * D * 2 * 3];
   for (int i = threadIdx.x; i < 64 * D * 2; i += blockDim.x) tile[i] = (__bf16)(seed * (float)i);
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -328,7 +362,7 @@ __global__ __launch_bounds__(512, 1) void mfma_lds(Stamp* out, float* sink, int 
       }
     }
     r = s0[0] + s1[5];
-  } else if (valu) {
+  } else if (valu && wave >= 4) {
     float s[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = seed * (float)(threadIdx.x + i);
@@ -337,8 +371,9 @@ __global__ __launch_bounds__(512, 1) void mfma_lds(Stamp* out, float* sink, int 
     const float cc = seed * 0.5f;
     c0 = __builtin_amdgcn_s_memtime();
     r0 = __builtin_amdgcn_s_memrealtime();
-    // 16 MFMAs per MFMA-wave iteration: 2 mix iterations (56 VALU)
-    for (int it = 0; it < 2 * iters; ++it) {
+    // 16 MFMAs per MFMA-wave iteration: 1 mix iteration (57 VALU), the
+    // attention kernels' ratio
+    for (int it = 0; it < iters; ++it) {
       const float m = l0 * 1e-30f;
 #pragma unroll
       for (int i = 0; i < 14; i += 2) {
@@ -356,6 +391,106 @@ __global__ __launch_bounds__(512, 1) void mfma_lds(Stamp* out, float* sink, int 
   const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
   sink[blockIdx.x * blockDim.x + threadIdx.x] = r;
   stamp_store(out, 8, c0, c1, r0, r1);
+}
+
+// ---------------------------------------------------------------------------
+// 4b. one wave per SIMD interleaving its own MFMAs with vector work
+// ---------------------------------------------------------------------------
+// Four waves (one per SIMD), each issuing 16 v_mfma_f32_32x32x16_bf16 per K
+// tile on 4 independent accumulators, with M softmax pairs per tile (per
+// pair: 2 fma, 2 exp, 2 add, 1 cvt_pk_bf16, 1 xor; 8 vector instructions)
+// on independent registers, scheduled as one MFMA then M/2 vector
+// instructions, 16 times.  The A operand comes
+//   LDSR 0: from registers;
+//   LDSR 1: one 1 KiB ds_read_b128 fragment per MFMA (32 queries per wave);
+//   LDSR 2: one fragment per two MFMAs against two query blocks (64 queries
+//           per wave: half the LDS bytes per flop).
+template <int M, int LDSR>
+__global__ __launch_bounds__(256, 1) void mfma_inwave(Stamp* out, float* sink, int iters,
+                                                      float seed) {
+  constexpr int D = 128;
+  // 32 KiB of K tiles, allocated as 96 KiB so that one work-group holds a CU
+  __shared__ __attribute__((aligned(16))) __bf16 tile[64 * D * 2 * 3];
+  for (int i = threadIdx.x; i < 64 * D * 2; i += blockDim.x) tile[i] = (__bf16)(seed * (float)i);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int ln = lane & 31, lh = lane >> 5;
+  bf16x8 qf[8], qg[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qf[ks][i] = (__bf16)(seed * (float)(lane + ks + i));
+      qg[ks][i] = (__bf16)(seed * (float)(lane - ks + 2 * i));
+    }
+  int koff[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koff[ks] = ln * D + (((2 * ks + lh) ^ (ln & 15)) * 8);
+  f32x16 acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = seed * (float)(threadIdx.x + 3 * i + 1);
+  float l0 = 0.f, l1 = 0.f;
+  unsigned pk = 0;
+  const float cc = seed * 0.5f;
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; it += 2) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const __bf16* kt = tile + t * 64 * D;
+      const float m = l0 * 1e-30f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        bf16x8 a0, a1;
+        if constexpr (LDSR == 0) {
+          a0 = qg[ks];
+          a1 = qg[7 - ks];
+        } else if constexpr (LDSR == 1) {
+          a0 = *(const bf16x8*)(kt + koff[ks]);
+          a1 = *(const bf16x8*)(kt + 32 * D + koff[ks]);
+        } else {
+          a0 = *(const bf16x8*)(kt + koff[ks]);
+          a1 = a0;
+        }
+        if (ks & 1) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, LDSR == 2 ? qg[ks] : qf[ks], acc1,
+                                                         0, 0, 0);
+        } else {
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], acc2, 0, 0, 0);
+          acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, LDSR == 2 ? qg[ks] : qf[ks], acc3,
+                                                         0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int pr = 0; pr < M; ++pr) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[(2 * pr) & 15], cc, m));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(x[(2 * pr + 1) & 15], cc, m));
+        const f32x2 v = {e0, e1};
+        pk ^= __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+        l0 += e0;
+        l1 += e1;
+      }
+      // schedule: the fragment reads a few ahead, then one MFMA and M / 2
+      // vector instructions at a time
+      if constexpr (LDSR != 0) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if constexpr (LDSR == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (LDSR == 2) {
+          if (i & 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(0x002, M / 2, 0);
+      }
+    }
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  sink[blockIdx.x * blockDim.x + threadIdx.x] =
+      acc0[0] + acc1[1] + acc2[2] + acc3[3] + l0 + l1 + (float)pk;
+  stamp_store(out, 4, c0, c1, r0, r1);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,6 +557,7 @@ extern "C" int mb_valu_rate(int op, int grid, int waves, int iters, void* stamps
     case 2: return (int)mb::launch(mb::valu_rate<2>, grid, blk, s, (mb::Stamp*)stamps, sink, iters, seed);
     case 3: return (int)mb::launch(mb::valu_rate<3>, grid, blk, s, (mb::Stamp*)stamps, sink, iters, seed);
     case 4: return (int)mb::launch(mb::valu_rate<4>, grid, blk, s, (mb::Stamp*)stamps, sink, iters, seed);
+    case 5: return (int)mb::launch(mb::valu_rate<5>, grid, blk, s, (mb::Stamp*)stamps, sink, iters, seed);
     default: return (int)hipErrorInvalidValue;
   }
 }
@@ -454,6 +590,20 @@ extern "C" int mb_mfma_lds(int grid, int mfma_waves, int valu, int iters, void* 
   if (mfma_waves < 0 || mfma_waves > 8 || grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
   return (int)mb::launch(mb::mfma_lds, grid, 512, s, (mb::Stamp*)stamps, sink, iters, mfma_waves,
                          valu, 1e-3f);
+}
+
+extern "C" int mb_mfma_inwave(int m, int ldsr, int grid, int iters, void* stamps, float* sink,
+                              hipStream_t s) {
+  if (grid < 1 || iters < 2) return (int)hipErrorInvalidValue;
+  mb::Stamp* st = (mb::Stamp*)stamps;
+#define MB_IW(M, L)                                                                          \
+  if (m == M && ldsr == L)                                                                   \
+    return (int)mb::launch(mb::mfma_inwave<M, L>, grid, 256, s, st, sink, iters, 1e-3f);
+  MB_IW(0, 0) MB_IW(4, 0) MB_IW(6, 0) MB_IW(8, 0) MB_IW(10, 0)
+  MB_IW(0, 1) MB_IW(4, 1) MB_IW(6, 1) MB_IW(8, 1) MB_IW(10, 1)
+  MB_IW(0, 2) MB_IW(4, 2) MB_IW(6, 2) MB_IW(8, 2) MB_IW(10, 2)
+#undef MB_IW
+  return (int)hipErrorInvalidValue;
 }
 
 extern "C" int mb_mfma_one(int dtype, const void* A, const void* B, const float* C, float* D,

@@ -15,6 +15,10 @@ Rows:
             accumulators), accumulators in VGPRs or AGPRs, alone and with a
             softmax-mix wave on the same SIMD (and that wave's cycles per
             vector instruction);
+  mfma+valu in one wave
+            cycles per MFMA when one wave per SIMD issues its MFMAs with 0-5
+            independent vector instructions after each, the A operand from
+            registers or LDS;
   lds       LDS bytes read per cycle per compute unit (ds_read_b128,
             ds_read_b64, ds_read_b64_tr_b16) with 4, 8 or 16 waves;
   mfma+lds  cycles per MFMA when its A operand is a 1 KiB ds_read_b128
@@ -34,8 +38,18 @@ if ROOT not in sys.path:
 
 
 def _stamps(buf, waves):
-    a = buf.cpu().numpy().reshape(-1, waves, 4).astype(np.float64)
-    return a   # [grid][waves][c0, c1, r0, r1]
+    # [grid][waves][c0, c1, r0, r1, hw_id, xcc_id, -, -]
+    return buf.cpu().numpy().reshape(-1, waves, 8)
+
+
+def _placement(s):
+    """Work-groups per compute unit (max over units), from each work-group's
+    first wave: HW_ID bits 15:8 (engine, array, CU) and XCC_ID."""
+    hw = s[:, 0, 4].astype(np.int64)
+    xcc = s[:, 0, 5].astype(np.int64)
+    key = (xcc & 0xF) * 256 + ((hw >> 8) & 0xFF)
+    _, counts = np.unique(key, return_counts=True)
+    return int(counts.max())
 
 
 class Runner:
@@ -46,7 +60,8 @@ class Runner:
         self.lib = microbench.load()
         self.grid = grid
         self.stream = torch.cuda.current_stream().cuda_stream
-        self.stamps = torch.zeros(grid * 16 * 4, dtype=torch.int64, device="cuda")
+        self.stamps = torch.zeros(grid * 16 * 8, dtype=torch.int64, device="cuda")
+        self.max_per_cu = 0
         self.sink = torch.zeros(grid * 1024, dtype=torch.float32, device="cuda")
 
     def _launch(self, fn, *args):
@@ -56,27 +71,31 @@ class Runner:
                 raise RuntimeError("launch failed: hipError %d" % st)
         self.torch.cuda.synchronize()
 
+    def _read(self, waves):
+        s = _stamps(self.stamps[:self.grid * waves * 8], waves)
+        self.max_per_cu = max(self.max_per_cu, _placement(s))
+        return (s[:, :, 1] - s[:, :, 0]).astype(np.float64), (s[:, :, 3] - s[:, :, 2]).astype(
+            np.float64)
+
     def valu(self, op, waves, iters):
         self._launch(self.lib.mb_valu_rate, op, self.grid, waves, iters)
-        s = _stamps(self.stamps[:self.grid * waves * 4], waves)
-        cyc = s[:, :, 1] - s[:, :, 0]
-        rt = s[:, :, 3] - s[:, :, 2]
-        return cyc, rt
+        return self._read(waves)
 
     def pair(self, acc, mfma_waves, valu, iters):
         self._launch(self.lib.mb_mfma_pair, acc, self.grid, mfma_waves, valu, iters)
-        s = _stamps(self.stamps[:self.grid * 8 * 4], 8)
-        return s[:, :, 1] - s[:, :, 0], s[:, :, 3] - s[:, :, 2]
+        return self._read(8)
 
     def lds(self, kind, waves, iters):
         self._launch(self.lib.mb_lds_read, kind, self.grid, waves, iters)
-        s = _stamps(self.stamps[:self.grid * waves * 4], waves)
-        return s[:, :, 1] - s[:, :, 0], s[:, :, 3] - s[:, :, 2]
+        return self._read(waves)
 
     def mfma_lds(self, mfma_waves, valu, iters):
         self._launch(self.lib.mb_mfma_lds, self.grid, mfma_waves, valu, iters)
-        s = _stamps(self.stamps[:self.grid * 8 * 4], 8)
-        return s[:, :, 1] - s[:, :, 0], s[:, :, 3] - s[:, :, 2]
+        return self._read(8)
+
+    def inwave(self, m, ldsr, iters):
+        self._launch(self.lib.mb_mfma_inwave, m, ldsr, self.grid, iters)
+        return self._read(4)
 
 
 def _mhz(cyc, rt):
@@ -85,7 +104,8 @@ def _mhz(cyc, rt):
 
 
 VALU_OPS = [(0, "v_fma_f32", 16), (1, "v_exp_f32", 16), (2, "v_add_f32", 16),
-            (3, "v_cvt_pk_bf16_f32", 8), (4, "softmax mix (fma, exp, add, cvt, xor)", 57)]
+            (3, "v_cvt_pk_bf16_f32", 8), (5, "v_exp_f32 and v_fma_f32 alternating", 16),
+            (4, "softmax mix (fma, exp, add, cvt, xor)", 57)]
 
 
 def run(quick=False):
@@ -120,14 +140,25 @@ def run(quick=False):
                      "%.2f cycles per MFMA per SIMD" % mf2, _mhz(cyc, rt)))
         cyc, rt = r.pair(acc, 4, 1, iters)
         mf = np.median(cyc[:, :4]) / (iters * 32)
-        va = np.median(cyc[:, 4:]) / (4 * iters * 57)
+        va = np.median(cyc[:, 4:]) / (2 * iters * 57)
         rows.append(("mfma", "32x32x16 bf16, " + accname, "+1 softmax wave/SIMD",
                      "%.2f cycles per MFMA; partner %.2f cycles per vector instruction "
-                     "(228 per 32 MFMAs)" % (mf, va), _mhz(cyc, rt)))
+                     "(114 per 32 MFMAs)" % (mf, va), _mhz(cyc, rt)))
     cyc, rt = r.pair(0, 0, 1, 4000 // k)
-    va = np.median(cyc[:, 4:]) / (4 * (4000 // k) * 57)
+    va = np.median(cyc[:, 4:]) / (2 * (4000 // k) * 57)
     rows.append(("mfma", "(softmax wave alone)", "1 wave/SIMD",
                  "%.2f cycles per vector instruction" % va, _mhz(cyc[:, 4:], rt[:, 4:])))
+
+    # one wave per SIMD interleaving its own MFMAs and vector work
+    for ldsr, lname in ((0, "A in registers"), (1, "A from LDS, 1 read per MFMA"),
+                        (2, "A from LDS, 1 read per 2 MFMAs")):
+        for m in (0, 4, 6, 8, 10):
+            iters = 8000 // k
+            cyc, rt = r.inwave(m, ldsr, iters)
+            mf = np.median(cyc.max(axis=1)) / (iters * 16)
+            rows.append(("mfma+valu in one wave", "32x32x16 bf16, " + lname,
+                         "1 wave/SIMD, %d vector per MFMA" % (m // 2),
+                         "%.2f cycles per MFMA" % mf, _mhz(cyc, rt)))
 
     # LDS read bandwidth
     for kind, name, nbytes in ((0, "ds_read_b128", 1024), (1, "ds_read_b64", 512),
@@ -149,11 +180,11 @@ def run(quick=False):
         txt = "%.2f cycles per MFMA per SIMD (%.1f LDS bytes per cycle per CU)" % (
             mf, 4 * 1024 / mf)
         if valu:
-            va = np.median(cyc[:, 4:]) / (2 * iters * 57)
-            txt += "; partner %.2f cycles per vector instruction" % va
+            va = np.median(cyc[:, 4:]) / (iters * 57)
+            txt += "; partner %.2f cycles per vector instruction (57 per 16 MFMAs)" % va
         rows.append(("mfma+lds", "32x32x16 bf16, A from ds_read_b128", label, txt,
                      _mhz(cyc, rt)))
-    return props, rows
+    return props, rows, r.max_per_cu
 
 
 def main():
@@ -165,12 +196,13 @@ def main():
     if not torch.cuda.is_available():
         print("microbench needs a GPU", file=sys.stderr)
         sys.exit(1)
-    props, rows = run(args.quick)
+    props, rows, per_cu = run(args.quick)
     lines = ["# gfx950 microbenchmarks", "",
              "Command: `python -m microbench.run%s`" % (" --quick" if args.quick else ""), "",
              "Device: %s, %d compute units; one work-group per compute unit; figures in shader "
-             "clock cycles (s_memtime), median over work-groups." % (props.name,
-                                                                   props.multi_processor_count),
+             "clock cycles (s_memtime), median over work-groups; at most %d work-group(s) "
+             "shared a compute unit in any run (HW_ID / XCC_ID)." % (
+                 props.name, props.multi_processor_count, per_cu),
              "", "| unit | what | waves | result | clock MHz |", "|---|---|---|---|---|"]
     for row in rows:
         lines.append("| %s | %s | %s | %s | %.0f |" % row)

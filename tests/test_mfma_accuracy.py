@@ -6,20 +6,26 @@ v_mfma_f32_32x32x64_f8f6f4 (64 products per instruction, d/64 instructions
 chained through the fp32 accumulator), and the fp8 LSE tolerance in
 parity_common.py is derived from this instruction's error model:
 
-    |D - D_exact| <= EPS_E4M3_MFMA * sum_k |a_k b_k| + 2^-23 * (|C| + |D_exact|)
+    |D - (sum_k a_k b_k + C)| <= EPS_E4M3_MFMA * 2^e + 2^-23 * (|C| + |D_exact|),
+    e = floor(log2 max_k |a_k b_k|)
 
 (the second term is ordinary binary32 rounding of the accumulator).  The
-model's constant EPS_E4M3_MFMA is the largest ratio
-|D - D_exact - (fp32 terms)| / sum_k |a_k b_k| seen on these operands,
+error is bounded by the largest product's binade, not by the sum of the
+magnitudes: measured on 2M outputs of this instruction the ratio
+|error| / sum_k |a_k b_k| kept growing with the sample (a heavy tail), while
+|error| / 2^e stopped at 2^-11.04 with and without outliers and with a
+nonzero accumulator -- the worst case of 64 products each placed on a grid
+of 2^(e - 16) before an exact sum (64 half-steps = 2^(e - 11)).  The model's
+constant EPS_E4M3_MFMA is the largest |error - fp32 terms| / 2^e seen,
 rounded up to a power of two.  This test measures it on seeded e4m3 codes
 drawn as the fp8 workloads draw them (N(0,1), per-block amax / 448
 quantisation, with and without 0.1% x20 outliers), for one instruction with
-a zero accumulator and for the d = 128 chain of two, and fails if the
-model's constant does not cover what the hardware does.  It prints the
-measured ratios.
+a zero accumulator and for the d = 128 chain of two (bound: the sum of the
+two instructions' terms), and fails if the hardware exceeds the model.  It
+prints the measured ratios, and the ratio to sum_k |a_k b_k| for reference.
 
-The bf16 instruction (v_mfma_f32_32x32x16_bf16) is measured the same way
-for reference (its products are exact in binary32).
+The bf16 instruction (v_mfma_f32_32x32x16_bf16) is measured against the
+same kind of model for reference (its products are exact in binary32).
 
 A layout check comes first: small-integer operands, whose products and
 sums are exact in fp32, must give D exactly; that fixes which operand
@@ -56,14 +62,23 @@ def _e4m3_rows(wid, rows, outliers, d=64):
     return x["q"].reshape(rows, d), x["k"].reshape(rows, d)
 
 
-def _check(label, d_gpu, exact, absprod, c, eps):
+def _binade(x):
+    """2^floor(log2 x) for x > 0 (1 where x is 0: no products, no error)."""
+    return np.where(x > 0, 2.0 ** np.floor(np.log2(np.where(x > 0, x, 1.0))), 1.0)
+
+
+def _check(label, d_gpu, exact, scale_ref, absprod, c, eps):
+    """scale_ref: the model's per-output unit (2^e, or a sum of them for a
+    chain)."""
     fp32_part = U32 * (np.abs(c) + np.abs(exact))
     excess = np.maximum(np.abs(d_gpu - exact) - fp32_part, 0.0)
-    ratio = excess / np.maximum(absprod, 1e-300)
-    raw = np.abs(d_gpu - exact) / np.maximum(absprod, 1e-300)
-    print("%s: max |D - exact| / sum|a b| = %.3e (after the fp32 terms %.3e, = 2^%.2f); "
-          "model constant %.3e" % (label, raw.max(), ratio.max(), np.log2(max(ratio.max(), 1e-30)),
-                                   eps), flush=True)
+    ratio = excess / scale_ref
+    by_sum = np.abs(d_gpu - exact) / np.maximum(absprod, 1e-300)
+    print("%s: max (|D - exact| - fp32 terms) / 2^e = %.3e (= 2^%.2f; 99.99th percentile "
+          "%.3e) over %d outputs; model constant %.3e; for reference max |D - exact| / "
+          "sum|a b| = %.3e"
+          % (label, ratio.max(), np.log2(max(ratio.max(), 1e-30)), np.quantile(ratio, 0.9999),
+             ratio.size, eps, by_sum.max()), flush=True)
     assert ratio.max() <= eps, label
 
 
@@ -96,7 +111,7 @@ def test_layout_exact_on_small_integers():
 
 @pytest.mark.parametrize("outliers", [False, True])
 def test_e4m3_single_instruction(outliers):
-    n = 256
+    n = 1024
     qa, kb = _e4m3_rows(101 + outliers, n * 32, outliers)
     a, b = kb.reshape(n, 32, 64), qa.reshape(n, 32, 64)
     fa, fb = e4m3fn_bits_to_float64(a), e4m3fn_bits_to_float64(b)
@@ -104,14 +119,16 @@ def test_e4m3_single_instruction(outliers):
     d = _mfma("e4m3", a, b, c)
     exact = np.einsum("pmk,pnk->pmn", fa, fb)
     absprod = np.einsum("pmk,pnk->pmn", np.abs(fa), np.abs(fb))
-    _check("e4m3 one MFMA, outliers=%d" % outliers, d, exact, absprod, c, EPS_E4M3_MFMA)
+    pmax = np.abs(fa[:, :, None, :] * fb[:, None, :, :]).max(-1)
+    _check("e4m3 one MFMA, outliers=%d" % outliers, d, exact, _binade(pmax), absprod, c,
+           EPS_E4M3_MFMA)
 
 
 @pytest.mark.parametrize("outliers", [False, True])
 def test_e4m3_d128_chain(outliers):
     # the d = 128 score: two instructions, the second accumulating onto the
     # first's fp32 result, as in the kernels' S^T = K Q^T
-    n = 256
+    n = 1024
     qa, kb = _e4m3_rows(103 + outliers, n * 32, outliers, d=128)
     a, b = kb.reshape(n, 32, 128), qa.reshape(n, 32, 128)
     fa, fb = e4m3fn_bits_to_float64(a), e4m3fn_bits_to_float64(b)
@@ -122,9 +139,11 @@ def test_e4m3_d128_chain(outliers):
                d1.astype(np.float32))
     exact = np.einsum("pmk,pnk->pmn", fa, fb)
     absprod = np.einsum("pmk,pnk->pmn", np.abs(fa), np.abs(fb))
+    p1 = np.abs(fa[:, :, None, :64] * fb[:, None, :, :64]).max(-1)
+    p2 = np.abs(fa[:, :, None, 64:] * fb[:, None, :, 64:]).max(-1)
     # the chain's fp32 terms: one rounding of d1 and one of d2
-    _check("e4m3 d=128 chain, outliers=%d" % outliers, d2, exact, absprod,
-           np.abs(d1) + np.abs(d1), EPS_E4M3_MFMA)
+    _check("e4m3 d=128 chain, outliers=%d" % outliers, d2, exact, _binade(p1) + _binade(p2),
+           absprod, np.abs(d1) + np.abs(d1), EPS_E4M3_MFMA)
 
 
 def test_bf16_single_instruction():
@@ -137,4 +156,5 @@ def test_bf16_single_instruction():
     d = _mfma("bf16", a, b, c)
     exact = np.einsum("pmk,pnk->pmn", fa, fb)
     absprod = np.einsum("pmk,pnk->pmn", np.abs(fa), np.abs(fb))
-    _check("bf16 one MFMA", d, exact, absprod, c, EPS_BF16_MFMA)
+    pmax = np.abs(fa[:, :, None, :] * fb[:, None, :, :]).max(-1)
+    _check("bf16 one MFMA", d, exact, _binade(pmax), absprod, c, EPS_BF16_MFMA)
