@@ -7,14 +7,16 @@ marshals arguments.  There is no CPU fallback: without the built library the
 import of the binding raises.
 """
 
-from ._binding import (ATTN_ERR_HIP, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_OK,
-                       AttnError, attn_bwd, attn_fp8_quantize, attn_fwd, attn_fwd_fp8,
+from ._binding import (ATTN_BWD_NOALLOC_MAX_ROWS, ATTN_ERR_HIP, ATTN_ERR_INVALID_ARG,
+                       ATTN_ERR_UNSUPPORTED, ATTN_OK, AttnError, attn_bwd, attn_bwd_noalloc,
+                       attn_fp8_quantize, attn_fwd, attn_fwd_fp8,
                        attn_fwd_fp8_2pass, attn_fwd_fp8_gqa, attn_fwd_fp8_varlen, attn_fwd_gqa, attn_fwd_varlen,
                        attn_status_string, attn_version, lib_path, load_library)
 
 __all__ = [
     "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_HIP", "AttnError",
     "attn_fwd", "attn_fwd_fp8", "attn_fwd_gqa", "attn_fwd_varlen", "attn_fwd_fp8_gqa",
-    "attn_fwd_fp8_varlen", "attn_fwd_fp8_2pass", "attn_bwd", "attn_fp8_quantize", "attn_status_string", "attn_version",
+    "attn_fwd_fp8_varlen", "attn_fwd_fp8_2pass", "attn_bwd", "attn_bwd_noalloc",
+    "ATTN_BWD_NOALLOC_MAX_ROWS", "attn_fp8_quantize", "attn_status_string", "attn_version",
     "lib_path", "load_library",
 ]

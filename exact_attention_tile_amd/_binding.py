@@ -60,6 +60,8 @@ def load_library():
     lib.attn_fwd_fp8_varlen.restype = i
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     lib.attn_bwd.restype = i
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.attn_bwd_noalloc.restype = i
     lib.attn_fwd_fp8_2pass.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.attn_fwd_fp8_2pass.restype = i
     lib.attn_fp8_quantize.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
@@ -175,6 +177,23 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale
                                  int(N), int(d), int(causal), float(scale), _stream(stream))
     if check and st != ATTN_OK:
         raise AttnError(st, "attn_bwd")
+    return st
+
+
+ATTN_BWD_NOALLOC_MAX_ROWS = 1 << 22
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, stream=None,
+                     check=True):
+    """bf16 backward with the library's static workspace (no allocation);
+    see attn_bwd_noalloc in include/attn.h (B * H * N <=
+    ATTN_BWD_NOALLOC_MAX_ROWS; calls on one GPU must not overlap)."""
+    st = load_library().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                         _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), int(B), int(H),
+                                         int(N), int(d), int(causal), float(scale),
+                                         _stream(stream))
+    if check and st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_noalloc")
     return st
 
 

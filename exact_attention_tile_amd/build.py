@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libattn.so")
 
-SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "attn_bwd_bf16.hip", "attn_quant.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_fp8.hip", "attn_bwd_bf16.hip", "attn_quant.hip",
+           "attn_noalloc.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -246,6 +246,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
 int attn_fp8_quantize(const void* x, void* codes, float* descale, const unsigned* sign_bits,
                       int B, int N, int H, int d, hipStream_t stream);
 
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and results, with the D workspace
+ * in a static device array of the library instead of a caller's `delta`.
+ *   Arguments as for attn_bwd, without `delta`.
+ *   Limit: B * H * N <= ATTN_BWD_NOALLOC_MAX_ROWS (16 MiB of fp32 rows per
+ *   GPU, held from the library's load until the process ends); larger calls
+ *   return ATTN_ERR_UNSUPPORTED and launch nothing.
+ *   `stream` must belong to the current device (else ATTN_ERR_INVALID_ARG).
+ *   The first call on a device looks the array's device address up
+ *   (hipGetSymbolAddress); no call allocates or frees memory.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (different streams or host threads) race and must be serialised by
+ *   the caller.  Nothing in the array needs to start at zero (each call
+ *   writes every row it reads before reading it).
+ *   Errors: null pointers, B/H/N <= 0 -> ATTN_ERR_INVALID_ARG; the limit ->
+ *   ATTN_ERR_UNSUPPORTED (both before any HIP call); the rest as attn_bwd.
+ */
+#define ATTN_BWD_NOALLOC_MAX_ROWS (1 << 22)
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     int B, int H, int N, int d, int causal, float scale, hipStream_t stream);
+
 /* Static, human-readable name of a status code ("ATTN_OK", ...). */
 const char* attn_status_string(int status);
 

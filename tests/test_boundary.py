@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     assert set(names) == {"attn_fwd", "attn_fwd_fp8", "attn_fwd_gqa", "attn_fwd_varlen",
                           "attn_fwd_fp8_gqa", "attn_fwd_fp8_varlen", "attn_bwd", "attn_fp8_quantize",
-                          "attn_fwd_fp8_2pass",
+                          "attn_fwd_fp8_2pass", "attn_bwd_noalloc",
                           "attn_status_string", "attn_version"}
 
 
@@ -240,3 +240,30 @@ def call_quant(**kw):
 ])
 def test_quantize_arguments_rejected_on_host(lib, kw, status):
     assert call_quant(**kw) == status
+
+
+def call_bwd_na(**kw):
+    a = dict(GOOD, do=P + 0x7000, dq=P + 0x8000, dk=P + 0x9000, dv=P + 0xA000)
+    a.update(kw)
+    return eat.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                                a["scale"], None, check=False)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), eat.ATTN_ERR_INVALID_ARG), (dict(lse=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(do=0), eat.ATTN_ERR_INVALID_ARG), (dict(dv=0), eat.ATTN_ERR_INVALID_ARG),
+    (dict(B=0), eat.ATTN_ERR_INVALID_ARG), (dict(H=-1), eat.ATTN_ERR_INVALID_ARG),
+    (dict(N=0), eat.ATTN_ERR_INVALID_ARG),
+    # the static workspace holds ATTN_BWD_NOALLOC_MAX_ROWS rows of B * H * N
+    (dict(B=1, H=1, N=eat.ATTN_BWD_NOALLOC_MAX_ROWS + 1), eat.ATTN_ERR_UNSUPPORTED),
+    (dict(B=2, H=64, N=32769), eat.ATTN_ERR_UNSUPPORTED),
+])
+def test_bwd_noalloc_rejects_before_any_hip_call(lib, kw, status):
+    assert call_bwd_na(**kw) == status
+
+
+def test_bwd_noalloc_limit_matches_header():
+    text = open(HEADER).read()
+    assert "#define ATTN_BWD_NOALLOC_MAX_ROWS (1 << 22)" in text
+    assert eat.ATTN_BWD_NOALLOC_MAX_ROWS == 1 << 22
