@@ -101,7 +101,8 @@ def measured_counters(key, dtype):
       mfma_busy      SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x engine cycles
                      per XCD): the fraction of the launch the matrix cores
                      were busy, at the clock the chip held;
-      valu_per_mfma  SQ_INSTS_VALU / SQ_INSTS_MFMA;
+      valu_per_mfma  (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (the
+                     counter of vector instructions includes the MFMAs);
       lds_per_mfma   SQ_INSTS_LDS / SQ_INSTS_MFMA;
       clock_mhz      GRBM_GUI_ACTIVE / 8 XCDs / the launch's duration under
                      counters (the engine clock held over the launch);
@@ -119,11 +120,12 @@ def measured_counters(key, dtype):
                     return {
                         "source": "profiles/counters.txt (rocprofv3 --pmc, key %s)" % key,
                         "mfma_busy": round(v["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles), 4),
-                        "valu_per_mfma": round(v["SQ_INSTS_VALU"] / v["SQ_INSTS_MFMA"], 3),
+                        "valu_per_mfma": round((v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"]) /
+                                               v["SQ_INSTS_MFMA"], 3),
                         "lds_per_mfma": round(v["SQ_INSTS_LDS"] / v["SQ_INSTS_MFMA"], 3),
                         "clock_mhz": round(cycles / dur_ns * 1e3, 1),
                         "lds_bank_conflict_cycles": v["SQ_LDS_BANK_CONFLICT"],
-                        "sq_insts_valu": v["SQ_INSTS_VALU"],
+                        "sq_insts_valu": v["SQ_INSTS_VALU"] - v["SQ_INSTS_MFMA"],
                     }
     except (OSError, ValueError):
         return None
@@ -132,7 +134,7 @@ def measured_counters(key, dtype):
 
 def microbench_figures():
     """From the committed microbenchmark table (profiles/gfx950_microbench.md):
-    cycles per v_fma_f32 per SIMD with one wave per SIMD, and LDS bytes read
+    cycles per v_fma_f32 per SIMD with four waves per SIMD, and LDS bytes read
     per cycle per compute unit by ds_read_b128 and ds_read_b64_tr_b16 with
     16 waves.  None where the table is missing."""
     out = {"valu_cycles": None, "lds_b128": None, "lds_tr16": None}
@@ -146,7 +148,7 @@ def microbench_figures():
                     num = float(cells[3].split()[0])
                 except (ValueError, IndexError):
                     continue
-                if cells[0] == "valu" and cells[1] == "v_fma_f32" and cells[2].startswith("1 "):
+                if cells[0] == "valu" and cells[1] == "v_fma_f32" and cells[2].startswith("4 "):
                     out["valu_cycles"] = num
                 elif cells[0] == "lds" and cells[2].startswith("16 "):
                     if cells[1] == "ds_read_b128":
@@ -169,9 +171,10 @@ def algorithmic_bytes(w):
 def secondary_roofs(w, flops, achieved, ctr, mb):
     """The two on-chip roofs beside the matrix-core peak, in TFLOP/s of the
     metric's flops (each at the nominal 2.4 GHz, like the peak):
-      valu  the launch's vector ALU instructions (SQ_INSTS_VALU) issued back
-            to back at the measured cycles per instruction, spread over the
-            1024 SIMDs;
+      valu  the launch's vector ALU instructions other than MFMAs
+            (SQ_INSTS_VALU - SQ_INSTS_MFMA) issued back to back at the measured
+            cycles per v_fma_f32 with four waves per SIMD (the SIMD's full
+            rate), spread over the 1024 SIMDs;
       lds   the K and V operand reads from LDS: each 32-query wave reads the
             whole K and V tile for every tile it visits, 2 * d * e bytes per
             key, i.e. e / 64 bytes per flop (e = 2 bf16, 1 fp8), against the

@@ -139,6 +139,23 @@ def _update(path, key, fields, header):
         f.write("\n".join(lines) + "\n")
 
 
+SQ_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + " ".join(SQ) +
+          " --kernel-trace -d <out>/sq_{w} -o sq --output-format csv -- python3 /root/repo/bench.py"
+          " --workload {w} --steps 3 --warmup 1 --no-cpu-baseline{x}")
+CTR_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} --kernel-trace -d <out>/{n}_{w} "
+           "-o {n} --output-format csv -- python3 /root/repo/bench.py --workload {w} --steps 3 "
+           "--warmup 1 --no-cpu-baseline --copy-calibration{x}")
+
+
+def cmd_lines(a):
+    if a.cmds:
+        return [l.rstrip("\n") for l in open(a.cmds) if l.strip()]
+    x = (" " + a.bench_args) if a.bench_args else ""
+    return [SQ_CMD.format(w=a.workload, x=x),
+            CTR_CMD.format(c="FETCH_SIZE", n="fetch", w=a.workload, x=x),
+            CTR_CMD.format(c="WRITE_SIZE", n="write", w=a.workload, x=x)]
+
+
 def cmd_counters(a):
     import bench
     sq, sq_dur = counter_rows(a.sq)
@@ -153,13 +170,14 @@ def cmd_counters(a):
     dur_ns = sum(durs) / len(durs)
     cycles = vals["GRBM_GUI_ACTIVE"] / XCDS
     busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cycles)
-    vpm = vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"]
+    # SQ_INSTS_VALU counts the MFMAs too
+    vpm = (vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / vals["SQ_INSTS_MFMA"]
     clock = cycles / dur_ns * 1e3
     src = bench.kernel_source_hash(a.dtype)
     out = ["# " + a.title, "",
            "Three runs, one counter group each (counters are never combined with a trace "
            "other than the kernel trace):", "", "```"] + \
-          [l.rstrip("\n") for l in open(a.cmds) if l.strip()] + \
+          cmd_lines(a) + \
           ["```", "", "## Instruction mix and matrix-core activity (average per launch)", "",
            "| counter | value |", "|---|---|"]
     for c in SQ:
@@ -172,7 +190,8 @@ def cmd_counters(a):
             "- matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x cycles per XCD) = "
             "%.3f (%.1f busy cycles per MFMA instruction)" % (
                 SIMDS, busy, vals["SQ_VALU_MFMA_BUSY_CYCLES"] / vals["SQ_INSTS_MFMA"]),
-            "- vector ALU instructions per MFMA: %.2f; LDS instructions per MFMA: %.2f" % (
+            "- vector ALU instructions (other than MFMAs) per MFMA: %.2f; LDS instructions per "
+            "MFMA: %.2f" % (
                 vpm, vals["SQ_INSTS_LDS"] / vals["SQ_INSTS_MFMA"]),
             "", "## HBM traffic per launch", "",
             "The 1 GiB device copy that `--copy-calibration` runs after the timed region reads "
@@ -209,9 +228,12 @@ def main():
     t.add_argument("--title", required=True)
     t.add_argument("--out", required=True)
     c = sub.add_parser("counters")
-    for n in ("--sq", "--fetch", "--write", "--kernel", "--workload", "--key", "--cmds",
-              "--title", "--out"):
+    for n in ("--sq", "--fetch", "--write", "--kernel", "--workload", "--key", "--title", "--out"):
         c.add_argument(n, required=True)
+    c.add_argument("--cmds", default=None,
+                   help="file with the three rocprofv3 commands (default: the standard ones for "
+                        "--workload and --bench-args)")
+    c.add_argument("--bench-args", default="", help="extra bench.py arguments of the runs")
     c.add_argument("--dtype", required=True, choices=["bf16", "fp8", "quant", "bwd"])
     a = ap.parse_args()
     (cmd_trace if a.what == "trace" else cmd_counters)(a)

@@ -394,9 +394,9 @@ __global__ __launch_bounds__(512, 1) void mfma_lds(Stamp* out, float* sink, int 
 }
 
 // ---------------------------------------------------------------------------
-// 4b. one wave per SIMD interleaving its own MFMAs with vector work
+// 4b. waves interleaving their own MFMAs with vector work
 // ---------------------------------------------------------------------------
-// Four waves (one per SIMD), each issuing 16 v_mfma_f32_32x32x16_bf16 per K
+// Four or eight waves (one or two per SIMD), each issuing 16 v_mfma_f32_32x32x16_bf16 per K
 // tile on 4 independent accumulators, with M softmax pairs per tile (per
 // pair: 2 fma, 2 exp, 2 add, 1 cvt_pk_bf16, 1 xor; 8 vector instructions)
 // on independent registers, scheduled as one MFMA then M/2 vector
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(512, 1) void mfma_lds(Stamp* out, float* sink, int 
 //   LDSR 2: one fragment per two MFMAs against two query blocks (64 queries
 //           per wave: half the LDS bytes per flop).
 template <int M, int LDSR>
-__global__ __launch_bounds__(256, 1) void mfma_inwave(Stamp* out, float* sink, int iters,
+__global__ __launch_bounds__(512, 1) void mfma_inwave(Stamp* out, float* sink, int iters,
                                                       float seed) {
   constexpr int D = 128;
   // 32 KiB of K tiles, allocated as 96 KiB so that one work-group holds a CU
@@ -490,7 +490,73 @@ __global__ __launch_bounds__(256, 1) void mfma_inwave(Stamp* out, float* sink, i
   const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
   sink[blockIdx.x * blockDim.x + threadIdx.x] =
       acc0[0] + acc1[1] + acc2[2] + acc3[3] + l0 + l1 + (float)pk;
-  stamp_store(out, 4, c0, c1, r0, r1);
+  stamp_store(out, blockDim.x >> 6, c0, c1, r0, r1);
+}
+
+// ---------------------------------------------------------------------------
+// 4c. issue cost of tile loads
+// ---------------------------------------------------------------------------
+// Eight waves; the first `loaders` of them each issue L 1 KiB loads per
+// round (64 lanes x 16 bytes, consecutive), then wait for them, then the
+// work-group meets at a barrier: the attention kernels' tile-load pattern.
+// KIND 0: global_load_lds_dwordx4 (to LDS through M0), 1: global_load_dwordx4
+// into registers.  Per wave: cycles from the first issue to the last
+// (issue) and from there to the completed wait (drain), summed over rounds.
+// Each work-group reads its own 32 KiB slice per round of a buffer of
+// `nbytes` (a multiple of 32 KiB), wrapping around.
+template <int KIND, int L>
+__global__ __launch_bounds__(512, 1) void tile_loads(Stamp* out, float* sink, const char* src,
+                                                     long long nbytes, int loaders, int iters) {
+  MB_RESERVE_LDS(iters);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const unsigned lds0 = (unsigned)(size_t)((MB_LDS unsigned char*)mb_pad);
+  unsigned long long t_issue = 0, t_drain = 0, t_lgkm = 0;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const long long slices = nbytes / 32768;
+  for (int it = 0; it < iters; ++it) {
+    if (wave < loaders) {
+      const long long slice = ((long long)blockIdx.x * iters + it) % slices;
+      const char* base = src + slice * 32768 + (long long)wave * L * 1024;
+      const unsigned m0 = __builtin_amdgcn_readfirstlane(lds0 + (unsigned)(wave * L * 1024) % 65536u);
+      const unsigned long long a = __builtin_amdgcn_s_memtime();
+      if constexpr (KIND == 0) {
+#pragma unroll
+        for (int i = 0; i < L; ++i)
+          asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0 + i * 1024),
+                       "v"((unsigned)(lane * 16 + i * 1024)), "s"(base)
+                       : "memory");
+      } else {
+        // register loads: issued together and waited for in the same asm
+        // block (so no output register is live while its load is in
+        // flight); "issue" then also covers the wait
+#pragma unroll
+        for (int i = 0; i < L; i += 4) {
+          u32x4 v0, v1, v2, v3;
+          const unsigned o = (unsigned)(lane * 16 + i * 1024);
+          asm volatile("global_load_dwordx4 %0, %4, %8\n\tglobal_load_dwordx4 %1, %5, %8\n\t"
+                       "global_load_dwordx4 %2, %6, %8\n\tglobal_load_dwordx4 %3, %7, %8\n\t"
+                       "s_waitcnt vmcnt(0)"
+                       : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+                       : "v"(o), "v"(o + 1024), "v"(o + 2048), "v"(o + 3072), "s"(base)
+                       : "memory");
+          acc ^= v0 ^ v1 ^ v2 ^ v3;
+        }
+      }
+      const unsigned long long b = __builtin_amdgcn_s_memtime();
+      // an LDS-counter wait first: does the LDS DMA count against it?
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const unsigned long long b2 = __builtin_amdgcn_s_memtime();
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      const unsigned long long c = __builtin_amdgcn_s_memtime();
+      t_issue += b - a;
+      t_lgkm += b2 - b;
+      t_drain += c - b2;
+    }
+    __builtin_amdgcn_s_barrier();
+  }
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3]);
+  stamp_store(out, 8, t_issue, t_drain, t_lgkm, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -592,17 +658,33 @@ extern "C" int mb_mfma_lds(int grid, int mfma_waves, int valu, int iters, void* 
                          valu, 1e-3f);
 }
 
-extern "C" int mb_mfma_inwave(int m, int ldsr, int grid, int iters, void* stamps, float* sink,
-                              hipStream_t s) {
-  if (grid < 1 || iters < 2) return (int)hipErrorInvalidValue;
+extern "C" int mb_mfma_inwave(int m, int ldsr, int waves, int grid, int iters, void* stamps,
+                              float* sink, hipStream_t s) {
+  if (grid < 1 || iters < 2 || (waves != 4 && waves != 8)) return (int)hipErrorInvalidValue;
   mb::Stamp* st = (mb::Stamp*)stamps;
 #define MB_IW(M, L)                                                                          \
   if (m == M && ldsr == L)                                                                   \
-    return (int)mb::launch(mb::mfma_inwave<M, L>, grid, 256, s, st, sink, iters, 1e-3f);
+    return (int)mb::launch(mb::mfma_inwave<M, L>, grid, waves * 64, s, st, sink, iters, 1e-3f);
   MB_IW(0, 0) MB_IW(4, 0) MB_IW(6, 0) MB_IW(8, 0) MB_IW(10, 0)
   MB_IW(0, 1) MB_IW(4, 1) MB_IW(6, 1) MB_IW(8, 1) MB_IW(10, 1)
   MB_IW(0, 2) MB_IW(4, 2) MB_IW(6, 2) MB_IW(8, 2) MB_IW(10, 2)
 #undef MB_IW
+  return (int)hipErrorInvalidValue;
+}
+
+extern "C" int mb_tile_loads(int kind, int per_wave, int loaders, int grid, int iters,
+                             const void* src, long long nbytes, void* stamps, float* sink,
+                             hipStream_t s) {
+  if (grid < 1 || iters < 1 || loaders < 1 || loaders > 8 || nbytes < 32768 ||
+      nbytes % 32768 != 0 || loaders * per_wave > 32)
+    return (int)hipErrorInvalidValue;
+  mb::Stamp* st = (mb::Stamp*)stamps;
+  const char* p = (const char*)src;
+#define MB_TL(K, Lw)                                                                           \
+  if (kind == K && per_wave == Lw)                                                             \
+    return (int)mb::launch(mb::tile_loads<K, Lw>, grid, 512, s, st, sink, p, nbytes, loaders, iters);
+  MB_TL(0, 2) MB_TL(0, 4) MB_TL(0, 8) MB_TL(1, 4) MB_TL(1, 8)
+#undef MB_TL
   return (int)hipErrorInvalidValue;
 }
 

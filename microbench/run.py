@@ -93,9 +93,23 @@ class Runner:
         self._launch(self.lib.mb_mfma_lds, self.grid, mfma_waves, valu, iters)
         return self._read(8)
 
-    def inwave(self, m, ldsr, iters):
-        self._launch(self.lib.mb_mfma_inwave, m, ldsr, self.grid, iters)
-        return self._read(4)
+    def tile_loads(self, kind, per_wave, loaders, iters):
+        if not hasattr(self, "src"):
+            self.src = self.torch.zeros(512 << 20, dtype=self.torch.uint8, device="cuda")
+        for _ in range(2):
+            st = self.lib.mb_tile_loads(kind, per_wave, loaders, self.grid, iters,
+                                        self.src.data_ptr(), self.src.numel(),
+                                        self.stamps.data_ptr(), self.sink.data_ptr(), self.stream)
+            if st != 0:
+                raise RuntimeError("launch failed: hipError %d" % st)
+        self.torch.cuda.synchronize()
+        s = _stamps(self.stamps[:self.grid * 8 * 8], 8)
+        return (s[:, :loaders, 0].astype(np.float64), s[:, :loaders, 1].astype(np.float64),
+                s[:, :loaders, 2].astype(np.float64))
+
+    def inwave(self, m, ldsr, iters, waves=4):
+        self._launch(self.lib.mb_mfma_inwave, m, ldsr, waves, self.grid, iters)
+        return self._read(waves)
 
 
 def _mhz(cyc, rt):
@@ -149,16 +163,30 @@ def run(quick=False):
     rows.append(("mfma", "(softmax wave alone)", "1 wave/SIMD",
                  "%.2f cycles per vector instruction" % va, _mhz(cyc[:, 4:], rt[:, 4:])))
 
-    # one wave per SIMD interleaving its own MFMAs and vector work
-    for ldsr, lname in ((0, "A in registers"), (1, "A from LDS, 1 read per MFMA"),
-                        (2, "A from LDS, 1 read per 2 MFMAs")):
-        for m in (0, 4, 6, 8, 10):
-            iters = 8000 // k
-            cyc, rt = r.inwave(m, ldsr, iters)
-            mf = np.median(cyc.max(axis=1)) / (iters * 16)
-            rows.append(("mfma+valu in one wave", "32x32x16 bf16, " + lname,
-                         "1 wave/SIMD, %d vector per MFMA" % (m // 2),
-                         "%.2f cycles per MFMA" % mf, _mhz(cyc, rt)))
+    # one or two waves per SIMD, each interleaving its own MFMAs and vector work
+    for waves in (4, 8):
+        for ldsr, lname in ((0, "A in registers"), (1, "A from LDS, 1 read per MFMA"),
+                            (2, "A from LDS, 1 read per 2 MFMAs")):
+            for m in (0, 4, 6, 8, 10):
+                iters = 8000 // k
+                cyc, rt = r.inwave(m, ldsr, iters, waves)
+                mf = np.median(cyc.max(axis=1)) / (iters * 16 * (waves // 4))
+                rows.append(("mfma+valu in one wave", "32x32x16 bf16, " + lname,
+                             "%d wave(s)/SIMD, %d vector per MFMA" % (waves // 4, m // 2),
+                             "%.2f cycles per MFMA per SIMD" % mf, _mhz(cyc, rt)))
+
+    # tile loads: 32 KiB per round per work-group, as the attention kernels load a K/V tile
+    for kind, per_wave, loaders in ((0, 8, 4), (0, 4, 8), (0, 2, 8), (1, 8, 4), (1, 4, 8)):
+        iters = 400 // k
+        iss, drn, lgkm = r.tile_loads(kind, per_wave, loaders, iters)
+        name = "global_load_lds_dwordx4 (to LDS)" if kind == 0 else "global_load_dwordx4 (to VGPRs)"
+        txt = ("issue %.0f, then an lgkmcnt(0) wait %.0f, then the vmcnt(0) drain %.0f cycles "
+               "per wave per round" % (np.median(iss) / iters, np.median(lgkm) / iters,
+                                       np.median(drn) / iters)
+               if kind == 0 else "issue and wait %.0f cycles per wave per round"
+               % (np.median(iss) / iters))
+        rows.append(("tile loads", name, "%d loader waves x %d KiB" % (loaders, per_wave), txt,
+                     float("nan")))
 
     # LDS read bandwidth
     for kind, name, nbytes in ((0, "ds_read_b128", 1024), (1, "ds_read_b64", 512),
