@@ -19,7 +19,10 @@ _LIB = None
 
 
 def lib_path():
-    return os.path.join(_HERE, "libattn.so")
+    """The in-tree libattn.so, or the library named by EXACT_ATTN_LIB (the
+    tests use this to run the host-side checks against the sanitizer build,
+    libattn_hostcheck.so)."""
+    return os.environ.get("EXACT_ATTN_LIB") or os.path.join(_HERE, "libattn.so")
 
 
 class AttnError(RuntimeError):

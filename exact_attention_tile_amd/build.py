@@ -54,5 +54,31 @@ def build(verbose=False):
     return LIB
 
 
+HOSTCHECK_LIB = os.path.join(PKG, "libattn_hostcheck.so")
+HOSTCHECK_SOURCES = ["attn_api.cpp", "attn_noalloc.hip", "host_check_stubs.cpp"]
+
+
+def build_host_check(verbose=False):
+    """The C ABI's host code with the address and undefined-behaviour
+    sanitizers (host side only; stub launchers, no kernels), for running the
+    argument-validation tests on the CPU: libattn_hostcheck.so."""
+    srcs = [os.path.join(CSRC, s) for s in HOSTCHECK_SOURCES]
+    tmp = HOSTCHECK_LIB + ".tmp"
+    flags = ["--offload-arch=gfx950", "-O1", "-g", "-std=c++17", "-fPIC", "-shared",
+             "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+    cmd = [hipcc()] + flags + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + srcs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, out))
+    os.replace(tmp, HOSTCHECK_LIB)
+    return HOSTCHECK_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
