@@ -188,12 +188,23 @@ def _check_varlen(w, inp, out, causal, rows, skip=()):
         assert_bf16_ok(error_figures(go, gr, gl, grl), label)
 
 
+# H a multiple of 8 with B <= 128 takes the rank-ordered mapping (sequences
+# ranked by length on the device, longest first, ties by index; B > 64 needs
+# the second candidate round); other shapes take the head-major or
+# tile-major mappings.  Short-sequence batches hold zero lengths and ties.
+_SHORT100 = tuple((7 * i) % 45 for i in range(100))
+_SHORT128 = tuple((11 * i + 3) % 37 for i in range(128))
+_SHORT129 = tuple((5 * i + 1) % 29 for i in range(129))
 VARLEN_EDGE = [("bf16", (300, 1, 0, 129, 64), 4, 2, 64), ("bf16", (1000, 17, 256, 1), 6, 3, 128),
-               ("fp8", (200, 1, 77), 4, 4, 128), ("fp8", (65, 0, 300), 4, 2, 64)]
+               ("fp8", (200, 1, 77), 4, 4, 128), ("fp8", (65, 0, 300), 4, 2, 64),
+               ("bf16", (300, 1, 0, 129, 64, 700), 8, 2, 128), ("fp8", (513, 33, 1, 250, 0), 16, 4, 64),
+               ("fp8", (200, 77, 1000), 8, 8, 128), ("bf16", _SHORT100, 8, 4, 64),
+               ("fp8", _SHORT128, 16, 2, 128), ("bf16", _SHORT129, 8, 8, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("dtype,lengths,H,Hkv,d", VARLEN_EDGE)
+@pytest.mark.parametrize("dtype,lengths,H,Hkv,d", VARLEN_EDGE,
+                         ids=["%s-B%d-H%d-Hkv%d-d%d" % (c[0], len(c[1]), c[2], c[3], c[4]) for c in VARLEN_EDGE])
 def test_varlen_edge_batches(dtype, lengths, H, Hkv, d, causal):
     w = Workload("varlen_%s" % dtype, 30 + len(lengths), len(lengths), H, max(lengths), d, dtype,
                  (causal,), Hkv=Hkv, lengths=lengths, outliers=(dtype == "fp8"))
