@@ -1,8 +1,12 @@
-// C ABI of the tiled exact attention forward (see include/attn.h).
+// C ABI of the tiled exact attention forward, its backward pass and the fp8
+// quantiser (declared in include/attn.h).
 //
 // Every argument is validated on the host before any HIP call; on error
-// nothing is launched.  On success exactly one kernel is enqueued on the
-// caller's stream; the library allocates, frees and synchronises nothing.
+// nothing is launched.  On success the entry point's kernels are enqueued on
+// the caller's stream in order: one for a single-pass forward, two for the
+// two-pass fp8 forward, three or four for the backward pass, four for the
+// quantiser.  The library allocates, frees and synchronises nothing; the
+// backward pass's workspace is the caller's.
 #include "attn.h"
 
 #include <hip/hip_runtime.h>

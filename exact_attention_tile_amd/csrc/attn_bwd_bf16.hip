@@ -990,6 +990,324 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pp_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK and dV together, one wave per SIMD: per (batch, head, 128 key rows).
+// Each of the 4 waves owns 32 keys: their K and V rows stay in registers
+// (the B operands of S and dP) and dK^T, dV^T (32 keys x D fp32) accumulate
+// in the accumulation registers, which a wave has to itself when it is
+// alone on its SIMD.  64-query Q / dO tiles stream through three LDS
+// buffers (with their lse and D values); the wave walks them in 32-query
+// blocks t and overlaps, within its own instruction stream, the vector work
+// of one block with the matrix-core work of the next:
+//   iteration t:  S_{t+1} = Q_{t+1} K^T, dP_{t+1} = dO_{t+1} V^T
+//                 (matrix cores) together with P_t, dS_t (vector ALU), then
+//                 dV^T += dO_t^T P_t, dK^T += Q_t^T dS_t.
+// Five products per (query, key) pair of the backward pass are here (S, dP,
+// dV, dK) or in the dQ kernel (S, dP again, dQ).  Tile j+1 is loaded two
+// iterations before its first use; one barrier per tile, after block 2j,
+// publishes it and frees the buffer of tile j-1 for tile j+2.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_1w_kernel(BwdParams p) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int NW = 4;
+  constexpr int BK = NW * 32, BQ = 64, NBUF = 3;
+  constexpr int NKS = D / 16, NDB = D / 32;
+  constexpr int TILE = BQ * D;
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * NBUF * TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 vsm[BK * D];        // the work-group's V rows
+  __shared__ __attribute__((aligned(16))) float rowv[NBUF][2][BQ];   // [buffer][lse2, D][query]
+  __bf16* qs_base = smem;                   // Q tiles:  [NBUF][BQ][D]
+  __bf16* gs_base = smem + NBUF * TILE;     // dO tiles: [NBUF][BQ][D]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
+  const int ln = lane & 31;
+  const int lh = lane >> 5;
+
+  int bh, kt;
+  bwd_work(p, p.n_ktiles, bh, kt);      // causal: low key tiles see the most queries
+  const int b = bh / p.H;
+  const int h = bh - b * p.H;
+  const int N = p.N;
+  const long long tok = (long long)p.H * D;
+  const long long head_base = ((long long)b * N * p.H + h) * D;
+  const int k0 = kt * BK;
+  const int kw0 = k0 + wave * 32;
+  const int mykey = kw0 + ln;
+  const int kr = mykey < N ? mykey : N - 1;
+
+  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
+  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
+  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
+  const __bf16* __restrict__ gg = (const __bf16*)p.dout + head_base;
+
+  // K^T fragments (B operand of S = Q K^T): lane (n = ln, h = lh) holds row
+  // mykey, columns 16 ks + 8 lh .. +7.  The V^T fragments (B operand of
+  // dP = dO V^T) are read from the work-group's V rows in LDS.
+  bf16x8 kf[NKS];
+  {
+    const u32x4* ks = (const u32x4*)(kg + (long long)kr * tok + 8 * lh);
+#pragma unroll
+    for (int i = 0; i < NKS; ++i) kf[i] = __builtin_bit_cast(bf16x8, ks[2 * i]);
+  }
+  const float c = p.c;
+
+  const int n_q_all = (N + BQ - 1) / BQ;
+  const int first = CAUSAL ? k0 / BQ : 0;
+  const int nt = n_q_all - first;           // >= 1: k0 < N
+  const int nblk = 2 * nt;
+
+  TileLoader<D, NW, BQ> ld;
+  ld.init(wave, lane, tok);
+  const unsigned lds_q = (unsigned)(size_t)((ATTN_LDS __bf16*)qs_base);
+  const unsigned lds_g = (unsigned)(size_t)((ATTN_LDS __bf16*)gs_base);
+  const float* __restrict__ lse_h = p.lse + (long long)bh * N;
+  const float* __restrict__ del_h = p.delta + (long long)bh * N;
+  float row_lse = 0.f, row_del = 0.f;
+  // tile j (local): Q, dO into buffer j % 3; its lse / D into registers of
+  // wave 0, written to LDS by store_rowv after the wait
+  auto load_tile = [&](int j) {
+    j = __builtin_amdgcn_readfirstlane(j);
+    const int q0t = (first + j) * BQ;
+    const unsigned nb = (unsigned)((j % NBUF) * TILE * 2);
+    ld.load(qg, tok, lds_q + nb, q0t, N);
+    ld.load(gg, tok, lds_g + nb, q0t, N);
+    if (wave == 0) {
+      const int r = min(q0t + lane, N - 1);
+      row_lse = lse_h[r];
+      row_del = del_h[r];
+    }
+  };
+  auto store_rowv = [&](int j) {
+    if (wave == 0) {
+      rowv[j % NBUF][0][lane] = row_lse * kLog2e;
+      rowv[j % NBUF][1][lane] = row_del;
+    }
+  };
+
+  int qoff[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qoff[ks] = ln * D + (((2 * ks + lh) ^ swz_b<D>(ln)) * 8);
+  TrOffsets<D, NDB> tro;
+  tro.init(lane);
+  const __bf16* vw = vsm + wave * 32 * D;   // the wave's 32 V rows
+
+  f32x16 dk[NDB], dv[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dk[db] = f32x16{};
+    dv[db] = f32x16{};
+  }
+  // S and dP of blocks t and t+1 (slot = block & 1); P and dS of blocks t
+  // and t-1 (the B operands of the update), same slots
+  f32x16 s[2], dp[2];
+  bf16x8 pf[2][2], dsf[2][2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      pf[sl][g] = bf16x8{};
+      dsf[sl][g] = bf16x8{};
+    }
+  constexpr int NU = 4 * NDB;             // update products: (g, db, dV | dK)
+  constexpr int UA = 4;                   // update operands read ahead
+  bf16x8 ua[NU];                          // update operands (transposed rows)
+  // update product u: g = u / (2 NDB), db = (u / 2) % NDB, dV (u even) or dK
+  // (u odd); its A operand is dO^T or Q^T of the block's rows 16 g .. +15
+  auto u_read = [&](int u, const __bf16* qb, const __bf16* gb) __attribute__((always_inline)) {
+    const int g = u / (2 * NDB), db = (u >> 1) % NDB;
+    ua[u] = tr_operand(((u & 1) ? qb : gb) + 16 * g * D, tro.lo[db], tro.hi[db]);
+  };
+  auto u_mfma = [&](int u, int sl) __attribute__((always_inline)) {
+    const int g = u / (2 * NDB), db = (u >> 1) % NDB;
+    if (u & 1)
+      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[u], dsf[sl][g], dk[db], 0, 0, 0);
+    else
+      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[u], pf[sl][g], dv[db], 0, 0, 0);
+  };
+
+  // S, dP of block 0 (buffer 0, rows 0-31) into slot 0
+  auto sd0 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 qa = *(const bf16x8*)(qs_base + qoff[ks]);
+      const bf16x8 ga = *(const bf16x8*)(gs_base + qoff[ks]);
+      const bf16x8 vb = *(const bf16x8*)(vw + qoff[ks]);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16{} : s[0], 0, 0, 0);
+      dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, ks == 0 ? f32x16{} : dp[0], 0, 0, 0);
+    }
+  };
+
+  // Iteration t = 2 j + SL of tile j (block t = rows 32 SL .. 32 SL + 31 of
+  // the tile): the update of block t-1, S and dP of block t+1, and P and dS
+  // of block t.  It is written as 2 NU regions of one matrix-core product
+  // each, in a fixed order (scheduling fences between regions):
+  //   regions 0 .. NU-1:     update products of block t-1 (P, dS of slot SN);
+  //   regions NU .. 2NU-1:   S, dP of block t+1, k-step by k-step (slot SN);
+  // with the vector work of block t (slot SL) spread over all of them: its
+  // 16 (query, key) values per lane go in 8 pairs, pair p taking regions
+  // 4p+1 (exponential), 4p+2 (dS) and 4p+3 (packing to bf16).  LDS operands
+  // are read ahead: update operands UA products ahead (the first UA in the
+  // previous iteration's last regions), S / dP operands two k-steps ahead,
+  // a quarter's lse and D values four regions ahead.  The buffer offsets pass
+  // through an empty asm so that each iteration forms its own LDS addresses
+  // (one per lane pattern; the dO tile and row offsets are immediates).
+  // Block -1 (before the first) is an update with P = dS = 0 on block 0's
+  // rows; after the last block the S, dP products read a stale buffer and
+  // are discarded.
+  auto iter = [&](auto masked_tag, auto slot_tag, int j) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr int SL = decltype(slot_tag)::value;
+    constexpr int SN = SL ^ 1;
+    constexpr int NR = 2 * NU;
+    constexpr int qb0 = 32 * SL;
+    const int q0 = (first + j) * BQ + qb0;
+    const int buf = j % NBUF;
+    int ecur = buf * TILE + qb0 * D;                                   // block t
+    int enxt = SL ? ((j + 1) % NBUF) * TILE : ecur + 32 * D;           // block t+1
+    int eprv = SL ? buf * TILE : (j > 0 ? ((j + NBUF - 1) % NBUF) * TILE + 32 * D : ecur);
+    asm volatile("" : "+s"(ecur), "+s"(enxt), "+s"(eprv));
+    const __bf16* qc = qs_base + ecur;
+    const __bf16* gc = gs_base + ecur;
+    const __bf16* qn = qs_base + enxt;
+    const __bf16* gn = gs_base + enxt;
+    const __bf16* qp = qs_base + eprv;
+    const __bf16* gp = gs_base + eprv;
+
+    bf16x8 qa[NKS], ga[NKS], vb[NKS];
+    f32x4 lv[4], dv4[4];
+    float pe[16], dsv[16];
+    auto rows = [&](int x) __attribute__((always_inline)) {
+      lv[x] = *(const f32x4*)&rowv[buf][0][qb0 + 8 * x + 4 * lh];
+      dv4[x] = *(const f32x4*)&rowv[buf][1][qb0 + 8 * x + 4 * lh];
+    };
+    // pair p = values 2p, 2p+1 (registers of quarter x = p / 2)
+    auto stage_exp = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 2 * p + i, x = r >> 2, e = r & 3;
+        float v = fast_exp2(__builtin_fmaf(s[SL][r], c, -lv[x][e]));
+        if constexpr (MASKED) {
+          const int q = q0 + 8 * x + 4 * lh + e;
+          if (q >= N || (CAUSAL && mykey > q)) v = 0.f;
+        }
+        pe[r] = v;
+      }
+    };
+    auto stage_ds = [&](int p) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 2 * p + i, x = r >> 2, e = r & 3;
+        dsv[r] = pe[r] * (dp[SL][r] - dv4[x][e]);
+      }
+    };
+    auto stage_pack = [&](int p) __attribute__((always_inline)) {
+      const int g = p >> 2, w = p & 3;
+      u32x4 wp = __builtin_bit_cast(u32x4, pf[SL][g]);
+      u32x4 wd = __builtin_bit_cast(u32x4, dsf[SL][g]);
+      wp[w] = pack_bf16x2(pe[2 * p], pe[2 * p + 1]);
+      wd[w] = pack_bf16x2(dsv[2 * p], dsv[2 * p + 1]);
+      // computed here, not where first used (after the tile's barrier)
+      asm volatile("" : "+v"(wp), "+v"(wd));
+      pf[SL][g] = __builtin_bit_cast(bf16x8, wp);
+      dsf[SL][g] = __builtin_bit_cast(bf16x8, wd);
+    };
+
+    rows(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      // reads ahead
+      if (r + UA < NU) u_read(r + UA, qp, gp);
+      if (r >= NU - 4 && r < NR - 4 && (r & 1) == 0) {
+        const int ks = (r - (NU - 4)) / 2;
+        qa[ks] = *(const bf16x8*)(qn + qoff[ks]);
+        ga[ks] = *(const bf16x8*)(gn + qoff[ks]);
+        vb[ks] = *(const bf16x8*)(vw + qoff[ks]);
+      }
+      if (r >= NR - UA) u_read(r - (NR - UA), qc, gc);   // the next iteration's first
+      if ((r & 7) == 5 && (r >> 3) < 3) rows((r >> 3) + 1);
+      // the region's product
+      if (r < NU) {
+        u_mfma(r, SN);
+      } else {
+        const int ks = (r - NU) >> 1;
+        if ((r & 1) == 0)
+          s[SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? f32x16{} : s[SN], 0, 0, 0);
+        else
+          dp[SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vb[ks], ks == 0 ? f32x16{} : dp[SN], 0, 0, 0);
+      }
+      // the vector work of block t
+      if ((r & 3) == 1) stage_exp(r >> 2);
+      if ((r & 3) == 2) stage_ds(r >> 2);
+      if ((r & 3) == 3) stage_pack(r >> 2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the update of the last block (a tile's second: slot 1), after the loop
+  auto last_update = [&](int t) __attribute__((always_inline)) {
+    int ecur = ((t >> 1) % NBUF) * TILE + 32 * D;
+    asm volatile("" : "+s"(ecur));
+    const __bf16* qc = qs_base + ecur;
+    const __bf16* gc = gs_base + ecur;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      if (u + UA < NU) u_read(u + UA, qc, gc);
+      u_mfma(u, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // the P / dS of tile j need the mask: causal diagonal (or keys after all
+  // its queries) or rows past N
+  auto tile_masked = [&](int j) {
+    const int q0 = (first + j) * BQ;
+    return (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
+  };
+  // tile j: its two blocks, with the barrier between them that publishes
+  // tile j+1 and frees the buffer of tile j-1 for tile j+2
+  auto tile = [&](auto masked_tag, int j) __attribute__((always_inline)) {
+    iter(masked_tag, std::integral_constant<int, 0>{}, j);
+    wait_vmem();                  // tile j+1 (loaded two iterations ago)
+    if (j + 1 < nt) store_rowv(j + 1);
+    __syncthreads();
+    if (j + 2 < nt) load_tile(j + 2);
+    iter(masked_tag, std::integral_constant<int, 1>{}, j);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+
+  {
+    TileLoader<D, NW, BK> ldv;
+    ldv.init(wave, lane, tok);
+    ldv.load(vg, tok, (unsigned)(size_t)((ATTN_LDS __bf16*)vsm), k0, N);
+  }
+  load_tile(0);
+  wait_vmem();
+  store_rowv(0);
+  __syncthreads();
+  if (nt > 1) load_tile(1);
+  sd0();
+#pragma unroll
+  for (int u = 0; u < UA; ++u) u_read(u, qs_base, gs_base);   // block -1: block 0's rows
+  // masked tiles are a prefix (causal) and possibly the last one
+  int j = 0;
+  for (; j + 1 < nt && tile_masked(j); ++j) tile(T_{}, j);
+  for (; j + 1 < nt; ++j) tile(F_{}, j);
+  if (tile_masked(nt - 1))
+    tile(T_{}, nt - 1);
+  else
+    tile(F_{}, nt - 1);
+  last_update(nblk - 1);
+
+  if (mykey < N) {
+    store_rows<NDB>((__bf16*)p.dk + head_base + (long long)mykey * tok, dk, p.scale, lh);
+    store_rows<NDB>((__bf16*)p.dv + head_base + (long long)mykey * tok, dv, 1.f, lh);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host-side launch (called by the C ABI in attn_api.cpp)
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
@@ -1001,12 +1319,12 @@ static hipError_t launch_bwd_t(BwdParams prm, hipStream_t stream) {
   const int grid = prm.B * prm.H * prm.n_tiles;
   e = launch_kernel(attn_bwd_dq_kernel<D, CAUSAL>, dim3(grid), dim3(512), stream, prm);
   if (e != hipSuccess) return e;
-  prm.n_ktiles = prm.n_tiles;
   if constexpr (D == 128) {
-    e = launch_kernel(attn_bwd_dkdv_pp_kernel<D, CAUSAL, 1, 64>, dim3(grid), dim3(512), stream, prm);
-    if (e != hipSuccess) return e;
-    return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, 2>, dim3(grid), dim3(512), stream, prm);
+    prm.n_ktiles = (prm.N + 127) / 128;
+    return launch_kernel(attn_bwd_dkdv_1w_kernel<D, CAUSAL>, dim3(prm.B * prm.H * prm.n_ktiles),
+                         dim3(256), stream, prm);
   } else {
+    prm.n_ktiles = prm.n_tiles;
     return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, 3>, dim3(grid), dim3(512), stream, prm);
   }
 }
