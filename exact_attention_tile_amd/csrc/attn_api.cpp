@@ -4,7 +4,7 @@
 // Every argument is validated on the host before any HIP call; on error
 // nothing is launched.  On success the entry point's kernels are enqueued on
 // the caller's stream in order: one for a single-pass forward, two for the
-// two-pass fp8 forward, three or four for the backward pass, four for the
+// two-pass fp8 forward, three for the backward pass, four for the
 // quantiser.  The library allocates, frees and synchronises nothing; the
 // backward pass's workspace is the caller's.
 #include "attn.h"

@@ -11,7 +11,7 @@
 //   dS = P * (dP - D),   dQ = scale dS K,   dK = scale dS^T Q.
 // Like the forward, the N x N matrices P, dP, dS never reach HBM.
 //
-// Three kernels (four at d = 128), enqueued in order on the caller's stream:
+// Three kernels, enqueued in order on the caller's stream:
 //   delta : D_i for every row (a dot product of two rows), into the caller's
 //           fp32 workspace [B][H][N];
 //   dQ    : one work-group per (batch, head, 256 queries); each wave owns 32
@@ -19,13 +19,17 @@
 //             S^T = K Q^T, dP^T = V dO^T (A = K / V rows, B = Q^T / dO^T in
 //             VGPRs), dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (A = K^T from
 //             transposing LDS reads, B = dS^T packed to bf16);
-//   dK/dV : one work-group per (batch, head, 256 keys); each wave owns 32
-//           key columns (its K and V rows in registers; at d = 128 dV and dK
-//           come from two kernels, see below) and streams 64-query Q / dO
-//           tiles (plus their lse and D values) through LDS:
+//   dK/dV : key-owned waves (lane = key) streaming 64-query Q / dO tiles
+//           (plus their lse and D values) through LDS:
 //             S = Q K^T, dP = dO V^T (A = Q / dO rows), dS = P (dP - D),
 //             dV^T += dO^T P, dK^T += Q^T dS (A = dO^T / Q^T from transposing
 //             LDS reads, B = P / dS packed to bf16).
+//           At d = 64 each of the 8 waves of a 256-key work-group does all
+//           of it for its 32 keys; at d = 128 the two waves of a SIMD share
+//           32 keys, one computing S, P and dV, the other dP, dS and dK
+//           (P passed through LDS).  S and dP are computed once per (query,
+//           key) pair here and once more in the dQ kernel: 7 products per
+//           pair where the chain rule has 5.
 // No atomics: each output element is produced by exactly one lane, so the
 // results are deterministic.  The lane ownership, the 32x32x16 bf16 MFMA
 // layouts and the key/query permutation of the packed operands are those of
@@ -457,19 +461,17 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV: per (batch, head, 256 key rows); 64-query Q / dO tiles.  Each of
-// the 8 waves (two per SIMD) owns 32 keys.  At D = 64 one kernel produces
-// both gradients (WANT = 3).  At D = 128 the K and V rows of a wave and two
-// 32 x 128 fp32 accumulators do not fit the 256 registers of a wave that
-// shares its SIMD, so two kernels run instead: dV (WANT = 1: S, P, dV^T) and
-// dK (WANT = 2: S, P, dP, dS, dK^T), which recompute S.
+// dK and dV at D = 64: per (batch, head, 256 key rows); 64-query Q / dO
+// tiles.  Each of the 8 waves (two per SIMD) owns 32 keys and keeps their K
+// and V rows and both 32 x 64 fp32 accumulators in registers (at D = 128
+// these do not fit the 256 registers of a wave that shares its SIMD:
+// attn_bwd_dkdv_pair_kernel below splits the work between two waves).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int WANT>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
-  static_assert(D == 64 || D == 128, "head dim");
-  static_assert(WANT >= 1 && WANT <= 3, "dV (1), dK (2) or both (3)");
-  constexpr bool DV = (WANT & 1) != 0;
-  constexpr bool DK = (WANT & 2) != 0;
+  static_assert(D == 64, "head dim 64 (128: attn_bwd_dkdv_pair_kernel)");
+  constexpr bool DV = true;
+  constexpr bool DK = true;
   constexpr int NW = 8;
   constexpr int BK = NW * 32, BQ = 64;
   constexpr int NKS = D / 16, NDB = D / 32;
@@ -713,315 +715,47 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV in the forward's two-group ping-pong, per (batch, head, 256 key
-// rows) with Q / dO tiles of BQ queries; the wave ownership and products are
-// those of attn_bwd_dkdv_kernel above.  Launched for the dV kernel at
-// D = 128 (WANT = 1, BQ = 64), where it is ~10% faster than the sequential
-// form; for dK (more registers: a 64-query tile spills) and at D = 64 the
-// sequential form is faster.  Waves 0-3 (group A) and 4-7 (group B, one
-// phase behind) alternate
-//   X_j (matrix cores): dV^T += dO_j^T P_j and / or dK^T += Q_j^T dS_j, then
-//                       S (and dP) of tile j+1;
-//   Y_j (vector ALU):   P (and dS) of tile j+1.
-// A tile is read in four phases (its S / dP, then its update), so Q and dO
-// tiles rotate through three LDS buffers, as do the tiles' lse and D values;
-// group A issues the loads of tile u+1 at the start of its matrix-core phase
-// 2u and waits for them at the end of phase 2u+1, when wave 0 also writes
-// the lse and D values to LDS.
-// ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, int WANT, int BQ>
-__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pp_kernel(BwdParams p) {
-  static_assert(D == 64 || D == 128, "head dim");
-  static_assert(WANT >= 1 && WANT <= 3, "dV (1), dK (2) or both (3)");
-  static_assert(BQ == 32 || BQ == 64, "query tile");
-  constexpr bool DV = (WANT & 1) != 0;
-  constexpr bool DK = (WANT & 2) != 0;
-  constexpr int NW = 8;
-  constexpr int BK = NW * 32;
-  constexpr int NQB = BQ / 32;           // 32-query blocks per tile
-  constexpr int NKS = D / 16, NDB = D / 32;
-  constexpr int TILE = BQ * D;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[6 * TILE];
-  __shared__ __attribute__((aligned(16))) float rowv[3][2][BQ];   // [buffer][lse2, D][query]
-  __bf16* qs_base = smem;                // Q tiles:  [3][BQ][D]
-  __bf16* gs_base = smem + 3 * TILE;     // dO tiles: [3][BQ][D]
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int grp = wave >> 2;
-  const int ln = lane & 31;
-  const int lh = lane >> 5;
-
-  int bh, kt;
-  bwd_work(p, p.n_ktiles, bh, kt);      // causal: low key tiles see the most queries
-  const int b = bh / p.H;
-  const int h = bh - b * p.H;
-  const int N = p.N;
-  const long long tok = (long long)p.H * D;
-  const long long head_base = ((long long)b * N * p.H + h) * D;
-  const int k0 = kt * BK;
-  const int kw0 = k0 + wave * 32;
-  const int mykey = kw0 + ln;
-  const int kr = mykey < N ? mykey : N - 1;
-
-  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
-  const __bf16* __restrict__ gg = (const __bf16*)p.dout + head_base;
-
-  // K^T and V^T fragments (B operands of S = Q K^T and dP = dO V^T): lane
-  // (n = ln, h = lh) holds row mykey, columns 16 ks + 8 lh .. +7
-  bf16x8 kf[NKS], vf[DK ? NKS : 1];
-  {
-    const u32x4* ks = (const u32x4*)(kg + (long long)kr * tok + 8 * lh);
-    const u32x4* vs = (const u32x4*)(vg + (long long)kr * tok + 8 * lh);
-#pragma unroll
-    for (int i = 0; i < NKS; ++i) {
-      kf[i] = __builtin_bit_cast(bf16x8, ks[2 * i]);
-      if constexpr (DK) vf[i] = __builtin_bit_cast(bf16x8, vs[2 * i]);
-    }
-#pragma unroll
-    for (int i = 0; i < NKS; ++i) {
-      loaded(kf[i]);
-      if constexpr (DK) loaded(vf[i]);
-    }
-  }
-  const float c = p.c;
-
-  const int n_q_all = (N + BQ - 1) / BQ;
-  const int first = CAUSAL ? k0 / BQ : 0;
-  const int nt = n_q_all > first ? n_q_all - first : 0;    // tiles of this work-group
-  // the wave's keys see tile t (local index) unless all its queries precede them
-  const int wfirst = CAUSAL ? max(kw0 / BQ - first, 0) : 0;
-  const bool wave_on = kw0 < N;
-
-  TileLoader<D, 4, BQ> ld;
-  ld.init(wave & 3, lane, tok);
-  const unsigned lds_q = (unsigned)(size_t)((ATTN_LDS __bf16*)qs_base);
-  const unsigned lds_g = (unsigned)(size_t)((ATTN_LDS __bf16*)gs_base);
-  const float* __restrict__ lse_h = p.lse + (long long)bh * N;
-  const float* __restrict__ del_h = p.delta + (long long)bh * N;
-  float row_lse = 0.f, row_del = 0.f;
-  // tile u (local): Q, dO into buffer u % 3; its lse / D into registers of
-  // wave 0 (lanes < BQ), written to LDS by store_rowv after the wait
-  auto load_tile = [&](int u) {
-    const int q0t = (first + u) * BQ;
-    const unsigned nb = (unsigned)((u % 3) * TILE * 2);
-    ld.load(qg, tok, lds_q + nb, q0t, N);
-    ld.load(gg, tok, lds_g + nb, q0t, N);
-    if (wave == 0 && lane < BQ) {
-      const int r = min(q0t + lane, N - 1);
-      row_lse = lse_h[r];
-      row_del = del_h[r];
-    }
-  };
-  auto store_rowv = [&](int u) {
-    if (wave == 0 && lane < BQ) {
-      rowv[u % 3][0][lane] = row_lse * kLog2e;
-      rowv[u % 3][1][lane] = row_del;
-    }
-  };
-
-  int qoff[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qoff[ks] = ln * D + (((2 * ks + lh) ^ swz_b<D>(ln)) * 8);
-  TrOffsets<D, NDB> tro;
-  tro.init(lane);
-
-  f32x16 dk[DK ? NDB : 1], dv[DV ? NDB : 1];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    if constexpr (DK) dk[db] = f32x16{};
-    if constexpr (DV) dv[db] = f32x16{};
-  }
-  f32x16 s[NQB], dp[DK ? NQB : 1];
-  bf16x8 pf[DV ? NQB : 1][2], dsf[DK ? NQB : 1][2];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    s[qb] = f32x16{};
-    if constexpr (DK) dp[qb] = f32x16{};
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      if constexpr (DV) pf[qb][g] = bf16x8{};
-      if constexpr (DK) dsf[qb][g] = bf16x8{};
-    }
-  }
-
-  // ---- X_u: the update of tile u, then S (and dP) of tile u+1
-  auto phase_x = [&](auto up_tag, auto sd_tag, int u) {
-    constexpr bool UP = decltype(up_tag)::value;
-    constexpr bool SD = decltype(sd_tag)::value;
-    __builtin_amdgcn_s_setprio(3);
-    if constexpr (UP) {
-      const __bf16* qt = qs_base + (u % 3) * TILE;
-      const __bf16* gt = gs_base + (u % 3) * TILE;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g) {
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const int rowb = (32 * qb + 16 * g) * D;
-            if constexpr (DV) {
-              const bf16x8 ga = tr_operand(gt + rowb, tro.lo[db], tro.hi[db]);
-              dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, pf[qb][g], dv[db], 0, 0, 0);
-            }
-            if constexpr (DK) {
-              const bf16x8 qa = tr_operand(qt + rowb, tro.lo[db], tro.hi[db]);
-              dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, dsf[qb][g], dk[db], 0, 0, 0);
-            }
-          }
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if constexpr (SD) {
-      const __bf16* qt = qs_base + ((u + 1) % 3) * TILE;
-      const __bf16* gt = gs_base + ((u + 1) % 3) * TILE;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-          const bf16x8 qa = *(const bf16x8*)(qt + qb * 32 * D + qoff[ks]);
-          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16{} : s[qb], 0, 0, 0);
-          if constexpr (DK) {
-            const bf16x8 ga = *(const bf16x8*)(gt + qb * 32 * D + qoff[ks]);
-            dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], ks == 0 ? f32x16{} : dp[qb], 0, 0, 0);
-          }
-        }
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // ---- Y_u: P (and dS) of tile u+1 (queries q0t ..), packed to bf16
-  auto phase_y = [&](auto masked_tag, int u) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int buf = (u + 1) % 3;
-    const int q0t = (first + u + 1) * BQ;
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      // register r holds query q0t + 32 qb + 8 (r/4) + 4 lh + r%4 of key mykey
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        u32x4 wp, wd;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int rb = 8 * g + 4 * half;                        // registers rb .. rb+3
-          const int qi = 32 * qb + 8 * (rb >> 2) + 4 * lh;        // their first tile row
-          const f32x4 lv = *(const f32x4*)&rowv[buf][0][qi];
-          float pv[4], dsv[4];
-          f32x4 dv4;
-          if constexpr (DK) dv4 = *(const f32x4*)&rowv[buf][1][qi];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            float pe = fast_exp2(__builtin_fmaf(s[qb][rb + x], c, -lv[x]));
-            if constexpr (MASKED) {
-              const int q = q0t + qi + x;
-              if (q >= N || (CAUSAL && mykey > q)) pe = 0.f;
-            }
-            pv[x] = pe;
-            if constexpr (DK) dsv[x] = pe * (dp[qb][rb + x] - dv4[x]);
-          }
-          if constexpr (DV) {
-            wp[2 * half] = pack_bf16x2(pv[0], pv[1]);
-            wp[2 * half + 1] = pack_bf16x2(pv[2], pv[3]);
-          }
-          if constexpr (DK) {
-            wd[2 * half] = pack_bf16x2(dsv[0], dsv[1]);
-            wd[2 * half + 1] = pack_bf16x2(dsv[2], dsv[3]);
-          }
-        }
-        if constexpr (DV) pf[qb][g] = __builtin_bit_cast(bf16x8, wp);
-        if constexpr (DK) dsf[qb][g] = __builtin_bit_cast(bf16x8, wd);
-      }
-    }
-  };
-
-  if (grp == 0 && nt > 0) load_tile(0);
-  wait_vmem();
-  if (nt > 0) store_rowv(0);
-  __syncthreads();
-
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  const int n_phases = 2 * nt + 2;
-  for (int ph = 0; ph < n_phases; ++ph) {
-    if (grp == 0 && (ph & 1) == 0) {
-      const int u = ph >> 1;
-      if (u + 1 < nt) load_tile(u + 1);
-    }
-    const int q = ph - grp;
-    if (q >= 0 && wave_on) {
-      if ((q & 1) == 0) {
-        const int u = (q >> 1) - 1;
-        const bool up = u >= wfirst && u < nt;
-        const bool sd = u + 1 >= wfirst && u + 1 < nt;
-        if (up && sd)
-          phase_x(T_{}, T_{}, u);
-        else if (sd)
-          phase_x(F_{}, T_{}, u);
-        else if (up)
-          phase_x(T_{}, F_{}, u);
-      } else {
-        const int u = (q - 3) / 2;
-        if (u + 1 >= wfirst && u + 1 < nt) {
-          const int q0t = (first + u + 1) * BQ;
-          if ((q0t + BQ > N) || (CAUSAL && q0t < kw0 + 31))
-            phase_y(T_{}, u);
-          else
-            phase_y(F_{}, u);
-        }
-      }
-    }
-    if (grp == 0 && (ph & 1) == 1) {
-      wait_vmem();
-      const int u = ph >> 1;
-      if (u + 1 < nt) store_rowv(u + 1);
-    }
-    __syncthreads();
-  }
-
-  if (mykey < N) {
-    if constexpr (DK) store_rows<NDB>((__bf16*)p.dk + head_base + (long long)mykey * tok, dk, p.scale, lh);
-    if constexpr (DV) store_rows<NDB>((__bf16*)p.dv + head_base + (long long)mykey * tok, dv, 1.f, lh);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// dK and dV together, one wave per SIMD: per (batch, head, 128 key rows).
-// Each of the 4 waves owns 32 keys: their K and V rows stay in registers
-// (the B operands of S and dP) and dK^T, dV^T (32 keys x D fp32) accumulate
-// in the accumulation registers, which a wave has to itself when it is
-// alone on its SIMD.  64-query Q / dO tiles stream through three LDS
-// buffers (with their lse and D values); the wave walks them in 32-query
-// blocks t and overlaps, within its own instruction stream, the vector work
-// of one block with the matrix-core work of the next:
-//   iteration t:  S_{t+1} = Q_{t+1} K^T, dP_{t+1} = dO_{t+1} V^T
-//                 (matrix cores) together with P_t, dS_t (vector ALU), then
-//                 dV^T += dO_t^T P_t, dK^T += Q_t^T dS_t.
-// Five products per (query, key) pair of the backward pass are here (S, dP,
-// dV, dK) or in the dQ kernel (S, dP again, dQ).  Tile j+1 is loaded two
-// iterations before its first use; one barrier per tile, after block 2j,
-// publishes it and frees the buffer of tile j-1 for tile j+2.
+// dK and dV with each key block's work split between the two waves of a
+// SIMD, per (batch, head, 128 key rows), streaming 64-query Q / dO tiles.
+// Wave w < 4 (the P wave) and wave w + 4 (the dS wave) own the same 32 keys
+// k0 + 32 w .. +31.  The P wave keeps their K rows (B operand) and dV^T:
+//   S = Q K^T,  P = exp2(S scale log2(e) - lse log2(e)),  dV^T += dO^T P,
+// and hands P (fp32) to the dS wave through LDS; the dS wave keeps their V
+// rows and dK^T:
+//   dP = dO V^T,  dS = P (dP - D),  dK^T += Q^T dS.
+// The two alternate, one phase apart (a barrier ends every phase):
+//   phase 2i+2:  P wave  dV(i), S(i+1)   (matrix cores)  | dS wave  dS(i)
+//   phase 2i+3:  P wave  P(i+1)          (vector ALU)    | dS wave  dK(i), dP(i+1)
+// (phase 0: S(0) | dP(0); phase 1: P(0) | -), so one wave of a SIMD issues
+// products while the other issues its vector work.  S and dP are computed
+// once per (query, key) pair.  Tile i is read in phases 2i .. 2i+3, so the Q
+// and dO tiles rotate through three LDS buffers: tile k+1 is loaded (Q by
+// the P waves, dO by the dS waves, lse by wave 0, D by wave 4) at the start
+// of phase 2k and waited for at the end of phase 2k+1.  The accumulation
+// order per key is the tiles', then 16-query groups, so the results do not
+// depend on the split.  Operands are read from LDS four products ahead; the
+// swizzled offsets of k-step ks and column block db are the first ones XOR
+// 16 ks and XOR 32 db (elements).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_1w_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
-  constexpr int NW = 4;
-  constexpr int BK = NW * 32, BQ = 64, NBUF = 3;
+  constexpr int KW = 4;                   // key groups of 32 (one per SIMD)
+  constexpr int BK = KW * 32, BQ = 64, NB = 3;
   constexpr int NKS = D / 16, NDB = D / 32;
   constexpr int TILE = BQ * D;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * NBUF * TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 vsm[BK * D];        // the work-group's V rows
-  __shared__ __attribute__((aligned(16))) float rowv[NBUF][2][BQ];   // [buffer][lse2, D][query]
-  __bf16* qs_base = smem;                   // Q tiles:  [NBUF][BQ][D]
-  __bf16* gs_base = smem + NBUF * TILE;     // dO tiles: [NBUF][BQ][D]
+  constexpr int PF = 4;                   // LDS operands read this many products ahead
+  __shared__ __attribute__((aligned(16))) __bf16 qsm[NB * TILE];       // Q tiles, 3 buffers
+  __shared__ __attribute__((aligned(16))) __bf16 gsm[2 * TILE];        // dO tiles, 2 buffers
+  __shared__ __attribute__((aligned(16))) __bf16 vsm[BK * D];          // the work-group's V rows
+  __shared__ __attribute__((aligned(16))) f32x4 pbuf[KW][8][64];   // [key group][(qb, quarter)][lane]
+  __shared__ __attribute__((aligned(16))) float rowv[NB][2][BQ];   // [buffer][lse2, D][query]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
+  const int role = wave >> 2;                                  // 0: P wave, 1: dS wave
+  const int kgrp = wave & 3;
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
@@ -1033,277 +767,286 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_1w_kernel(BwdParams p) {
   const long long tok = (long long)p.H * D;
   const long long head_base = ((long long)b * N * p.H + h) * D;
   const int k0 = kt * BK;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + kgrp * 32;
   const int mykey = kw0 + ln;
   const int kr = mykey < N ? mykey : N - 1;
-
-  const __bf16* __restrict__ qg = (const __bf16*)p.q + head_base;
-  const __bf16* __restrict__ kg = (const __bf16*)p.k + head_base;
-  const __bf16* __restrict__ vg = (const __bf16*)p.v + head_base;
-  const __bf16* __restrict__ gg = (const __bf16*)p.dout + head_base;
-
-  // K^T fragments (B operand of S = Q K^T): lane (n = ln, h = lh) holds row
-  // mykey, columns 16 ks + 8 lh .. +7.  The V^T fragments (B operand of
-  // dP = dO V^T) are read from the work-group's V rows in LDS.
-  bf16x8 kf[NKS];
-  {
-    const u32x4* ks = (const u32x4*)(kg + (long long)kr * tok + 8 * lh);
-#pragma unroll
-    for (int i = 0; i < NKS; ++i) kf[i] = __builtin_bit_cast(bf16x8, ks[2 * i]);
-  }
   const float c = p.c;
 
   const int n_q_all = (N + BQ - 1) / BQ;
   const int first = CAUSAL ? k0 / BQ : 0;
-  const int nt = n_q_all - first;           // >= 1: k0 < N
-  const int nblk = 2 * nt;
+  const int nt = n_q_all - first;                          // >= 1: k0 < N
+  const int n_phases = 2 * nt + 2;
 
-  TileLoader<D, NW, BQ> ld;
-  ld.init(wave, lane, tok);
-  const unsigned lds_q = (unsigned)(size_t)((ATTN_LDS __bf16*)qs_base);
-  const unsigned lds_g = (unsigned)(size_t)((ATTN_LDS __bf16*)gs_base);
-  const float* __restrict__ lse_h = p.lse + (long long)bh * N;
-  const float* __restrict__ del_h = p.delta + (long long)bh * N;
-  float row_lse = 0.f, row_del = 0.f;
-  // tile j (local): Q, dO into buffer j % 3; its lse / D into registers of
-  // wave 0, written to LDS by store_rowv after the wait
-  auto load_tile = [&](int j) {
-    j = __builtin_amdgcn_readfirstlane(j);
-    const int q0t = (first + j) * BQ;
-    const unsigned nb = (unsigned)((j % NBUF) * TILE * 2);
-    ld.load(qg, tok, lds_q + nb, q0t, N);
-    ld.load(gg, tok, lds_g + nb, q0t, N);
-    if (wave == 0) {
-      const int r = min(q0t + lane, N - 1);
-      row_lse = lse_h[r];
-      row_del = del_h[r];
-    }
+  // this wave's share of the tile loads: Q and lse (P waves; tile k+1 at
+  // the start of phase 2k, waited for at the end of phase 2k+1) or dO and D
+  // (dS waves; tile k+1 at the start of phase 2k+1, waited for at the end of
+  // phase 2k+2).  Q tile i is read in phases 2i .. 2i+3, dO tile i in phases
+  // 2i+1 and 2i+2, hence three Q buffers and two dO buffers.
+  const __bf16* __restrict__ src = (const __bf16*)(role ? p.dout : p.q) + head_base;
+  const float* __restrict__ rsrc = (role ? p.delta : p.lse) + (long long)bh * N;
+  TileLoader<D, KW, BQ> ld;
+  ld.init(kgrp, lane, tok);
+  const unsigned lds_dst = (unsigned)(size_t)((ATTN_LDS __bf16*)(role ? gsm : qsm));
+  const int nbuf = role ? 2 : NB;
+  float row_val = 0.f;
+  auto load_tile = [&](int u) {
+    const int q0t = (first + u) * BQ;
+    ld.load(src, tok, lds_dst + (unsigned)((u % nbuf) * TILE * 2), q0t, N);
+    if (kgrp == 0) row_val = rsrc[min(q0t + lane, N - 1)];
   };
-  auto store_rowv = [&](int j) {
-    if (wave == 0) {
-      rowv[j % NBUF][0][lane] = row_lse * kLog2e;
-      rowv[j % NBUF][1][lane] = row_del;
+  auto store_rowv = [&](int u) {
+    if (kgrp == 0) rowv[u % NB][role][lane] = role ? row_val : row_val * kLog2e;
+  };
+  // the tile loads and barriers every wave takes part in, around phase ph
+  auto phase_begin = [&](int ph) {
+    const int k = (ph - role) >> 1;
+    if (((ph - role) & 1) == 0 && ph >= role && k + 1 < nt) load_tile(k + 1);
+  };
+  auto phase_end = [&](int ph) {
+    const int k = (ph - 1 - role) >> 1;
+    if (((ph - 1 - role) & 1) == 0 && ph >= 1 + role) {
+      wait_vmem();
+      if (k + 1 < nt) store_rowv(k + 1);
     }
+    __syncthreads();
   };
 
-  int qoff[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qoff[ks] = ln * D + (((2 * ks + lh) ^ swz_b<D>(ln)) * 8);
-  TrOffsets<D, NDB> tro;
+  // element offsets: row reads (k-step 0) and transposing reads (column
+  // block 0); the others are these XOR 16 ks / XOR 32 db
+  const int qoff0 = ln * D + ((lh ^ swz_b<D>(ln)) * 8);
+  TrOffsets<D, 1> tro;
   tro.init(lane);
-  const __bf16* vw = vsm + wave * 32 * D;   // the wave's 32 V rows
 
-  f32x16 dk[NDB], dv[NDB];
+  // the B operand rows of this wave's keys: K in registers (P wave); V from
+  // the work-group's V rows in LDS (dS wave)
+  bf16x8 bf[NKS];
+  if (role == 0) {
+    const u32x4* rs = (const u32x4*)((const __bf16*)p.k + head_base + (long long)kr * tok + 8 * lh);
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    dk[db] = f32x16{};
-    dv[db] = f32x16{};
+    for (int i = 0; i < NKS; ++i) bf[i] = __builtin_bit_cast(bf16x8, rs[2 * i]);
+  } else {
+    TileLoader<D, KW, BK> ldv;
+    ldv.init(kgrp, lane, tok);
+    ldv.load((const __bf16*)p.v + head_base, tok, (unsigned)(size_t)((ATTN_LDS __bf16*)vsm), k0, N);
   }
-  // S and dP of blocks t and t+1 (slot = block & 1); P and dS of blocks t
-  // and t-1 (the B operands of the update), same slots
-  f32x16 s[2], dp[2];
-  bf16x8 pf[2][2], dsf[2][2];
-#pragma unroll
-  for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      pf[sl][g] = bf16x8{};
-      dsf[sl][g] = bf16x8{};
-    }
-  constexpr int NU = 4 * NDB;             // update products: (g, db, dV | dK)
-  constexpr int UA = 4;                   // update operands read ahead
-  bf16x8 ua[NU];                          // update operands (transposed rows)
-  // update product u: g = u / (2 NDB), db = (u / 2) % NDB, dV (u even) or dK
-  // (u odd); its A operand is dO^T or Q^T of the block's rows 16 g .. +15
-  auto u_read = [&](int u, const __bf16* qb, const __bf16* gb) __attribute__((always_inline)) {
-    const int g = u / (2 * NDB), db = (u >> 1) % NDB;
-    ua[u] = tr_operand(((u & 1) ? qb : gb) + 16 * g * D, tro.lo[db], tro.hi[db]);
-  };
-  auto u_mfma = [&](int u, int sl) __attribute__((always_inline)) {
-    const int g = u / (2 * NDB), db = (u >> 1) % NDB;
-    if (u & 1)
-      dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[u], dsf[sl][g], dk[db], 0, 0, 0);
-    else
-      dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ua[u], pf[sl][g], dv[db], 0, 0, 0);
-  };
 
-  // S, dP of block 0 (buffer 0, rows 0-31) into slot 0
-  auto sd0 = [&]() __attribute__((always_inline)) {
+  load_tile(0);
+  wait_vmem();
+  store_rowv(0);
+  if (role == 0) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 qa = *(const bf16x8*)(qs_base + qoff[ks]);
-      const bf16x8 ga = *(const bf16x8*)(gs_base + qoff[ks]);
-      const bf16x8 vb = *(const bf16x8*)(vw + qoff[ks]);
-      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], ks == 0 ? f32x16{} : s[0], 0, 0, 0);
-      dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb, ks == 0 ? f32x16{} : dp[0], 0, 0, 0);
-    }
-  };
+    for (int i = 0; i < NKS; ++i) loaded(bf[i]);
+  }
+  __syncthreads();
 
-  // Iteration t = 2 j + SL of tile j (block t = rows 32 SL .. 32 SL + 31 of
-  // the tile): the update of block t-1, S and dP of block t+1, and P and dS
-  // of block t.  It is written as 2 NU regions of one matrix-core product
-  // each, in a fixed order (scheduling fences between regions):
-  //   regions 0 .. NU-1:     update products of block t-1 (P, dS of slot SN);
-  //   regions NU .. 2NU-1:   S, dP of block t+1, k-step by k-step (slot SN);
-  // with the vector work of block t (slot SL) spread over all of them: its
-  // 16 (query, key) values per lane go in 8 pairs, pair p taking regions
-  // 4p+1 (exponential), 4p+2 (dS) and 4p+3 (packing to bf16).  LDS operands
-  // are read ahead: update operands UA products ahead (the first UA in the
-  // previous iteration's last regions), S / dP operands two k-steps ahead,
-  // a quarter's lse and D values four regions ahead.  The buffer offsets pass
-  // through an empty asm so that each iteration forms its own LDS addresses
-  // (one per lane pattern; the dO tile and row offsets are immediates).
-  // Block -1 (before the first) is an update with P = dS = 0 on block 0's
-  // rows; after the last block the S, dP products read a stale buffer and
-  // are discarded.
-  auto iter = [&](auto masked_tag, auto slot_tag, int j) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    constexpr int SL = decltype(slot_tag)::value;
-    constexpr int SN = SL ^ 1;
-    constexpr int NR = 2 * NU;
-    constexpr int qb0 = 32 * SL;
-    const int q0 = (first + j) * BQ + qb0;
-    const int buf = j % NBUF;
-    int ecur = buf * TILE + qb0 * D;                                   // block t
-    int enxt = SL ? ((j + 1) % NBUF) * TILE : ecur + 32 * D;           // block t+1
-    int eprv = SL ? buf * TILE : (j > 0 ? ((j + NBUF - 1) % NBUF) * TILE + 32 * D : ecur);
-    asm volatile("" : "+s"(ecur), "+s"(enxt), "+s"(eprv));
-    const __bf16* qc = qs_base + ecur;
-    const __bf16* gc = gs_base + ecur;
-    const __bf16* qn = qs_base + enxt;
-    const __bf16* gn = gs_base + enxt;
-    const __bf16* qp = qs_base + eprv;
-    const __bf16* gp = gs_base + eprv;
-
-    bf16x8 qa[NKS], ga[NKS], vb[NKS];
-    f32x4 lv[4], dv4[4];
-    float pe[16], dsv[16];
-    auto rows = [&](int x) __attribute__((always_inline)) {
-      lv[x] = *(const f32x4*)&rowv[buf][0][qb0 + 8 * x + 4 * lh];
-      dv4[x] = *(const f32x4*)&rowv[buf][1][qb0 + 8 * x + 4 * lh];
+  // S (P wave) or dP (dS wave) of tile u: 2 blocks of 32 queries, A = the
+  // tile's Q or dO rows, B = this wave's K or V rows
+  f32x16 acc2[2];
+  auto score = [&](auto role_tag, int u) __attribute__((always_inline)) {
+    constexpr int R = decltype(role_tag)::value;
+    int eb = (u % (R ? 2 : NB)) * TILE;
+    int qo = qoff0;
+    asm volatile("" : "+s"(eb), "+v"(qo));
+    const __bf16* t = (R ? gsm : qsm) + eb;
+    const __bf16* vt = vsm + kgrp * 32 * D;
+    constexpr int NP = 2 * NKS;           // products (ks, qb), ks-major
+    bf16x8 a[NP], vb[NKS];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      const int ks = i >> 1, qb = i & 1;
+      a[i] = *(const bf16x8*)(t + qb * 32 * D + (qo ^ (16 * ks)));
+      if constexpr (R == 1)
+        if (qb == 0) vb[ks] = *(const bf16x8*)(vt + (qo ^ (16 * ks)));
     };
-    // pair p = values 2p, 2p+1 (registers of quarter x = p / 2)
-    auto stage_exp = [&](int p) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 2 * p + i, x = r >> 2, e = r & 3;
-        float v = fast_exp2(__builtin_fmaf(s[SL][r], c, -lv[x][e]));
-        if constexpr (MASKED) {
-          const int q = q0 + 8 * x + 4 * lh + e;
-          if (q >= N || (CAUSAL && mykey > q)) v = 0.f;
-        }
-        pe[r] = v;
-      }
-    };
-    auto stage_ds = [&](int p) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = 2 * p + i, x = r >> 2, e = r & 3;
-        dsv[r] = pe[r] * (dp[SL][r] - dv4[x][e]);
-      }
-    };
-    auto stage_pack = [&](int p) __attribute__((always_inline)) {
-      const int g = p >> 2, w = p & 3;
-      u32x4 wp = __builtin_bit_cast(u32x4, pf[SL][g]);
-      u32x4 wd = __builtin_bit_cast(u32x4, dsf[SL][g]);
-      wp[w] = pack_bf16x2(pe[2 * p], pe[2 * p + 1]);
-      wd[w] = pack_bf16x2(dsv[2 * p], dsv[2 * p + 1]);
-      // computed here, not where first used (after the tile's barrier)
-      asm volatile("" : "+v"(wp), "+v"(wd));
-      pf[SL][g] = __builtin_bit_cast(bf16x8, wp);
-      dsf[SL][g] = __builtin_bit_cast(bf16x8, wd);
-    };
-
-    rows(0);
+    for (int i = 0; i < PF; ++i) rd(i);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      // reads ahead
-      if (r + UA < NU) u_read(r + UA, qp, gp);
-      if (r >= NU - 4 && r < NR - 4 && (r & 1) == 0) {
-        const int ks = (r - (NU - 4)) / 2;
-        qa[ks] = *(const bf16x8*)(qn + qoff[ks]);
-        ga[ks] = *(const bf16x8*)(gn + qoff[ks]);
-        vb[ks] = *(const bf16x8*)(vw + qoff[ks]);
-      }
-      if (r >= NR - UA) u_read(r - (NR - UA), qc, gc);   // the next iteration's first
-      if ((r & 7) == 5 && (r >> 3) < 3) rows((r >> 3) + 1);
-      // the region's product
-      if (r < NU) {
-        u_mfma(r, SN);
-      } else {
-        const int ks = (r - NU) >> 1;
-        if ((r & 1) == 0)
-          s[SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], ks == 0 ? f32x16{} : s[SN], 0, 0, 0);
-        else
-          dp[SN] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[ks], vb[ks], ks == 0 ? f32x16{} : dp[SN], 0, 0, 0);
-      }
-      // the vector work of block t
-      if ((r & 3) == 1) stage_exp(r >> 2);
-      if ((r & 3) == 2) stage_ds(r >> 2);
-      if ((r & 3) == 3) stage_pack(r >> 2);
+    for (int i = 0; i < NP; ++i) {
+      if (i + PF < NP) rd(i + PF);
+      const int ks = i >> 1, qb = i & 1;
+      const bf16x8 bop = R ? vb[ks] : bf[ks];
+      acc2[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bop, ks == 0 ? f32x16{} : acc2[qb], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // the update of the last block (a tile's second: slot 1), after the loop
-  auto last_update = [&](int t) __attribute__((always_inline)) {
-    int ecur = ((t >> 1) % NBUF) * TILE + 32 * D;
-    asm volatile("" : "+s"(ecur));
-    const __bf16* qc = qs_base + ecur;
-    const __bf16* gc = gs_base + ecur;
+  // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave) for tile u: A = the
+  // tile's dO or Q rows, transposed; B = the packed P or dS
+  f32x16 acc[NDB];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      if (u + UA < NU) u_read(u + UA, qc, gc);
-      u_mfma(u, 1);
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  bf16x8 pk[2][2];                        // [qb][g]: P or dS, packed
+  auto update = [&](auto role_tag, int u) __attribute__((always_inline)) {
+    constexpr int R = decltype(role_tag)::value;
+    int eb = (u % (R ? NB : 2)) * TILE;
+    int lo = tro.lo[0], hi = tro.hi[0];
+    asm volatile("" : "+s"(eb), "+v"(lo), "+v"(hi));
+    const __bf16* t = (R ? qsm : gsm) + eb;
+    constexpr int NP = 4 * NDB;           // products (qb, g, db)
+    bf16x8 a[NP];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      const int qb = i / (2 * NDB), g = (i / NDB) & 1, db = i % NDB;
+      a[i] = tr_operand(t + (32 * qb + 16 * g) * D, lo ^ (32 * db), hi ^ (32 * db));
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i + PF < NP) rd(i + PF);
+      const int qb = i / (2 * NDB), g = (i / NDB) & 1, db = i % NDB;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], pk[qb][g], acc[db], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  // the P / dS of tile j need the mask: causal diagonal (or keys after all
-  // its queries) or rows past N
-  auto tile_masked = [&](int j) {
-    const int q0 = (first + j) * BQ;
-    return (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
+  // register r of block qb holds query q0t + 32 qb + 8 (r/4) + 4 lh + r%4 of
+  // key mykey; quarter x = r/4 = 2 g + half.  The vector phases go group by
+  // group (qb, g), the LDS values of the next group read one group ahead.
+  auto p_values = [&](auto masked_tag, int u) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int buf = u % NB;
+    const int q0t = (first + u) * BQ;
+    f32x4 lv[4][2];                       // [group][half]
+    auto rd = [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        lv[gi][half] = *(const f32x4*)&rowv[buf][0][16 * gi + 8 * half + 4 * lh];
+    };
+    rd(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {      // gi = 2 qb + g
+      if (gi + 1 < 4) rd(gi + 1);
+      const int qb = gi >> 1, g = gi & 1;
+      u32x4 w;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int x = 2 * g + half;
+        f32x4 pe;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = fast_exp2(__builtin_fmaf(acc2[qb][4 * x + e], c, -lv[gi][half][e]));
+          if constexpr (MASKED) {
+            const int q = q0t + 16 * gi + 8 * half + 4 * lh + e;
+            if (q >= N || (CAUSAL && mykey > q)) v = 0.f;
+          }
+          pe[e] = v;
+        }
+        pbuf[kgrp][4 * qb + x][lane] = pe;
+        w[2 * half] = pack_bf16x2(pe[0], pe[1]);
+        w[2 * half + 1] = pack_bf16x2(pe[2], pe[3]);
+      }
+      pk[qb][g] = __builtin_bit_cast(bf16x8, w);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  // tile j: its two blocks, with the barrier between them that publishes
-  // tile j+1 and frees the buffer of tile j-1 for tile j+2
-  auto tile = [&](auto masked_tag, int j) __attribute__((always_inline)) {
-    iter(masked_tag, std::integral_constant<int, 0>{}, j);
-    wait_vmem();                  // tile j+1 (loaded two iterations ago)
-    if (j + 1 < nt) store_rowv(j + 1);
-    __syncthreads();
-    if (j + 2 < nt) load_tile(j + 2);
-    iter(masked_tag, std::integral_constant<int, 1>{}, j);
+  auto ds_values = [&](int u) __attribute__((always_inline)) {
+    const int buf = u % NB;
+    f32x4 dv4[4][2], pe[4][2];            // [group][half]
+    auto rd = [&](int gi) __attribute__((always_inline)) {
+      const int qb = gi >> 1, g = gi & 1;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        dv4[gi][half] = *(const f32x4*)&rowv[buf][1][16 * gi + 8 * half + 4 * lh];
+        pe[gi][half] = pbuf[kgrp][4 * qb + 2 * g + half][lane];
+      }
+    };
+    rd(0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      if (gi + 1 < 4) rd(gi + 1);
+      const int qb = gi >> 1, g = gi & 1;
+      u32x4 w;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int x = 2 * g + half;
+        float dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dsv[e] = pe[gi][half][e] * (acc2[qb][4 * x + e] - dv4[gi][half][e]);
+        w[2 * half] = pack_bf16x2(dsv[0], dsv[1]);
+        w[2 * half + 1] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+      pk[qb][g] = __builtin_bit_cast(bf16x8, w);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // tile u's P needs the mask: causal diagonal (or keys after all its
+  // queries) or rows past N
+  auto tile_masked = [&](int u) {
+    const int q0 = (first + u) * BQ;
+    return (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
 
-  {
-    TileLoader<D, NW, BK> ldv;
-    ldv.init(wave, lane, tok);
-    ldv.load(vg, tok, (unsigned)(size_t)((ATTN_LDS __bf16*)vsm), k0, N);
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  // Each loop iteration is one (matrix-core, vector) phase pair, so the
+  // accumulators keep their registers from phase to phase.
+  if (role == 0) {
+    // phase 0: S(0); phase 1: P(0); phase 2i+2: dV(i), S(i+1); phase 2i+3: P(i+1)
+    phase_begin(0);
+    __builtin_amdgcn_s_setprio(3);
+    score(R0{}, 0);
+    __builtin_amdgcn_s_setprio(0);
+    phase_end(0);
+    phase_begin(1);
+    if (tile_masked(0))
+      p_values(T_{}, 0);
+    else
+      p_values(F_{}, 0);
+    phase_end(1);
+    for (int i = 0; i + 1 < nt; ++i) {
+      phase_begin(2 * i + 2);
+      __builtin_amdgcn_s_setprio(3);
+      update(R0{}, i);
+      score(R0{}, i + 1);
+      __builtin_amdgcn_s_setprio(0);
+      phase_end(2 * i + 2);
+      phase_begin(2 * i + 3);
+      if (tile_masked(i + 1))
+        p_values(T_{}, i + 1);
+      else
+        p_values(F_{}, i + 1);
+      phase_end(2 * i + 3);
+    }
+    phase_begin(2 * nt);
+    update(R0{}, nt - 1);
+    phase_end(2 * nt);
+    phase_begin(2 * nt + 1);
+    phase_end(2 * nt + 1);
+  } else {
+    // phase 0: dP(0); phase 1: -; phase 2i+2: dS(i); phase 2i+3: dK(i), dP(i+1)
+    phase_begin(0);
+    __builtin_amdgcn_s_setprio(3);
+    score(R1{}, 0);
+    __builtin_amdgcn_s_setprio(0);
+    phase_end(0);
+    phase_begin(1);
+    phase_end(1);
+    for (int i = 0; i + 1 < nt; ++i) {
+      phase_begin(2 * i + 2);
+      ds_values(i);
+      phase_end(2 * i + 2);
+      phase_begin(2 * i + 3);
+      __builtin_amdgcn_s_setprio(3);
+      update(R1{}, i);
+      score(R1{}, i + 1);
+      __builtin_amdgcn_s_setprio(0);
+      phase_end(2 * i + 3);
+    }
+    phase_begin(2 * nt);
+    ds_values(nt - 1);
+    phase_end(2 * nt);
+    phase_begin(2 * nt + 1);
+    update(R1{}, nt - 1);
+    phase_end(2 * nt + 1);
   }
-  load_tile(0);
-  wait_vmem();
-  store_rowv(0);
-  __syncthreads();
-  if (nt > 1) load_tile(1);
-  sd0();
-#pragma unroll
-  for (int u = 0; u < UA; ++u) u_read(u, qs_base, gs_base);   // block -1: block 0's rows
-  // masked tiles are a prefix (causal) and possibly the last one
-  int j = 0;
-  for (; j + 1 < nt && tile_masked(j); ++j) tile(T_{}, j);
-  for (; j + 1 < nt; ++j) tile(F_{}, j);
-  if (tile_masked(nt - 1))
-    tile(T_{}, nt - 1);
-  else
-    tile(F_{}, nt - 1);
-  last_update(nblk - 1);
 
   if (mykey < N) {
-    store_rows<NDB>((__bf16*)p.dk + head_base + (long long)mykey * tok, dk, p.scale, lh);
-    store_rows<NDB>((__bf16*)p.dv + head_base + (long long)mykey * tok, dv, 1.f, lh);
+    __bf16* dst = (__bf16*)(role ? p.dk : p.dv) + head_base + (long long)mykey * tok;
+    store_rows<NDB>(dst, acc, role ? p.scale : 1.f, lh);
   }
 }
 
@@ -1321,11 +1064,11 @@ static hipError_t launch_bwd_t(BwdParams prm, hipStream_t stream) {
   if (e != hipSuccess) return e;
   if constexpr (D == 128) {
     prm.n_ktiles = (prm.N + 127) / 128;
-    return launch_kernel(attn_bwd_dkdv_1w_kernel<D, CAUSAL>, dim3(prm.B * prm.H * prm.n_ktiles),
-                         dim3(256), stream, prm);
+    return launch_kernel(attn_bwd_dkdv_pair_kernel<D, CAUSAL>, dim3(prm.B * prm.H * prm.n_ktiles),
+                         dim3(512), stream, prm);
   } else {
     prm.n_ktiles = prm.n_tiles;
-    return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, 3>, dim3(grid), dim3(512), stream, prm);
+    return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL>, dim3(grid), dim3(512), stream, prm);
   }
 }
 

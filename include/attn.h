@@ -39,8 +39,8 @@
  *     allocates nothing, frees nothing and never synchronises.  The
  *     single-pass forwards (attn_fwd, attn_fwd_fp8 and their grouped-query
  *     and variable-length forms) enqueue exactly one kernel on `stream`
- *     (0 = the null stream); attn_fwd_fp8_2pass enqueues two, attn_bwd three
- *     or four and attn_fp8_quantize four, in order on the same stream.
+ *     (0 = the null stream); attn_fwd_fp8_2pass enqueues two, attn_bwd
+ *     three and attn_fp8_quantize four, in order on the same stream.
  *   - Argument errors (ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED) are
  *     detected on the host before any HIP call; nothing is launched then.
  *     ATTN_ERR_HIP reports a failed launch: for a multi-kernel entry point
@@ -204,9 +204,8 @@ int attn_fwd_fp8_varlen(const void* q, const void* k, const void* v, void* o, fl
  *   delta            : fp32 [B][H][N], device, caller-owned workspace (the
  *                      library allocates nothing); written with D.
  *   B, H, N, d, causal, scale, stream : as for attn_fwd.
- * The kernels are enqueued on `stream` in order: D, dQ, then dK/dV (at
- * d = 128 dV and dK are separate launches); the results are deterministic
- * (no atomics).  Errors as for attn_fwd; null
+ * Three kernels are enqueued on `stream` in order: D, dQ, then dK and dV;
+ * the results are deterministic (no atomics).  Errors as for attn_fwd; null
  * dout/dq/dk/dv/delta is ATTN_ERR_INVALID_ARG.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -606,6 +606,78 @@ static hipError_t launch(void (*kernel)(KArgs...), int grid, int block, hipStrea
                          stream);
 }
 
+
+// ---------------------------------------------------------------------------
+// MFMA dependency: NCH accumulator chains in each wave, every MFMA reading
+// its chain's previous result as SrcC, the chains issued round-robin; one or
+// two waves per SIMD.  How many independent chains keep the matrix core
+// busy.
+// ---------------------------------------------------------------------------
+template <int NCH>
+__global__ __launch_bounds__(512, 1) void mfma_chain(Stamp* out, float* sink, int iters,
+                                                     float seed) {
+  MB_RESERVE_LDS(iters);
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(seed * (float)(threadIdx.x + i));
+    b[i] = (__bf16)(seed - (float)i);
+  }
+  f32x16 acc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) acc[c] = f32x16{};
+  __syncthreads();
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float r = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) r += acc[c][c];
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  stamp_store(out, blockDim.x >> 6, c0, c1, r0, r1);
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = r;
+}
+
+// ---------------------------------------------------------------------------
+// LDS read latency: each lane follows a chain of dependent reads through an
+// LDS table (the value read is the next byte address), one wave per SIMD;
+// KIND 0 ds_read_b32, 1 ds_read_b128 (the next address is the first dword).
+// ---------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void lds_latency(Stamp* out, float* sink, int iters) {
+  MB_RESERVE_LDS(iters);
+  __shared__ __attribute__((aligned(16))) unsigned tab[4096];   // 16 KiB
+  // entry i points 16 entries (64 bytes) further, wrapping: a lane's chain
+  // stays inside its own 16-byte column, lanes hit different banks
+  for (int i = threadIdx.x; i < 4096; i += blockDim.x) tab[i] = (unsigned)(((i + 16) & 4095) * 4);
+  __syncthreads();
+  unsigned addr = (unsigned)((threadIdx.x & 63) * 16);   // lane l starts at entry 4 l
+  const unsigned base = (unsigned)(size_t)((MB_LDS unsigned*)tab);
+  const unsigned long long c0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if constexpr (KIND == 0) {
+        asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(addr) : "v"(base + addr) : "memory");
+      } else {
+        u32x4 v;
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(base + addr) : "memory");
+        addr = v[0];
+      }
+    }
+  }
+  const unsigned long long c1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  stamp_store(out, blockDim.x >> 6, c0, c1, r0, r1);
+  sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)addr;
+}
 }  // namespace mb
 
 // ---------------------------------------------------------------------------
@@ -695,4 +767,27 @@ extern "C" int mb_mfma_one(int dtype, const void* A, const void* B, const float*
     return (int)mb::launch(mb::mfma_one_e4m3, n, 64, s, (const unsigned char*)A,
                            (const unsigned char*)B, C, D, n);
   return (int)mb::launch(mb::mfma_one_bf16, n, 64, s, (const __bf16*)A, (const __bf16*)B, C, D, n);
+}
+
+extern "C" int mb_mfma_chain(int nch, int waves, int grid, int iters, void* stamps, float* sink,
+                             hipStream_t s) {
+  if (grid < 1 || iters < 1 || (waves != 4 && waves != 8)) return (int)hipErrorInvalidValue;
+  mb::Stamp* st = (mb::Stamp*)stamps;
+  const int blk = waves * 64;
+  switch (nch) {
+    case 1: return (int)mb::launch(mb::mfma_chain<1>, grid, blk, s, st, sink, iters, 1e-3f);
+    case 2: return (int)mb::launch(mb::mfma_chain<2>, grid, blk, s, st, sink, iters, 1e-3f);
+    case 3: return (int)mb::launch(mb::mfma_chain<3>, grid, blk, s, st, sink, iters, 1e-3f);
+    case 4: return (int)mb::launch(mb::mfma_chain<4>, grid, blk, s, st, sink, iters, 1e-3f);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+extern "C" int mb_lds_latency(int kind, int grid, int iters, void* stamps, float* sink,
+                              hipStream_t s) {
+  if (grid < 1 || iters < 1) return (int)hipErrorInvalidValue;
+  mb::Stamp* st = (mb::Stamp*)stamps;
+  if (kind == 0) return (int)mb::launch(mb::lds_latency<0>, grid, 256, s, st, sink, iters);
+  if (kind == 1) return (int)mb::launch(mb::lds_latency<1>, grid, 256, s, st, sink, iters);
+  return (int)hipErrorInvalidValue;
 }

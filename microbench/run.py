@@ -111,6 +111,14 @@ class Runner:
         self._launch(self.lib.mb_mfma_inwave, m, ldsr, waves, self.grid, iters)
         return self._read(waves)
 
+    def chain(self, nch, waves, iters):
+        self._launch(self.lib.mb_mfma_chain, nch, waves, self.grid, iters)
+        return self._read(waves)
+
+    def lds_latency(self, kind, iters):
+        self._launch(self.lib.mb_lds_latency, kind, self.grid, iters)
+        return self._read(4)
+
 
 def _mhz(cyc, rt):
     ok = rt > 0
@@ -122,13 +130,39 @@ VALU_OPS = [(0, "v_fma_f32", 16), (1, "v_exp_f32", 16), (2, "v_add_f32", 16),
             (4, "softmax mix (fma, exp, add, cvt, xor)", 57)]
 
 
-def run(quick=False):
+def run(quick=False, only=None):
+    """All rows, or (only = list of "chain", "ldslat") just those groups."""
     import torch
+
+    def want(name):
+        return only is None or name in only
     props = torch.cuda.get_device_properties(0)
     grid = props.multi_processor_count
     r = Runner(grid)
     k = 4 if quick else 1
     rows = []
+
+    # MFMA dependency chains: cycles per MFMA with 1-4 chains per wave
+    if want("chain"):
+        for waves in (4, 8):
+            for nch in (1, 2, 3, 4):
+                iters = 2000 // k
+                cyc, rt = r.chain(nch, waves, iters)
+                mf = np.median(cyc.max(axis=1)) / (iters * 8 * nch * (waves // 4))
+                rows.append(("mfma chains", "32x32x16 bf16, %d chain(s) per wave" % nch,
+                             "%d wave(s)/SIMD" % (waves // 4),
+                             "%.2f cycles per MFMA per SIMD" % mf, _mhz(cyc, rt)))
+
+    # LDS read latency (dependent reads, one wave per SIMD)
+    if want("ldslat"):
+        for kind, name in ((0, "ds_read_b32"), (1, "ds_read_b128")):
+            iters = 2000 // k
+            cyc, rt = r.lds_latency(kind, iters)
+            rows.append(("lds latency", name, "1 wave/SIMD, dependent reads",
+                         "%.1f cycles per read" % (np.median(cyc) / (iters * 16)),
+                         _mhz(cyc, rt)))
+    if only:
+        return props, rows, r.max_per_cu
 
     # vector ALU issue rates
     for op, name, per in VALU_OPS:
@@ -219,12 +253,14 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=None)
     ap.add_argument("--quick", action="store_true", help="a quarter of the iterations")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated groups to run alone: chain, ldslat")
     args = ap.parse_args()
     import torch
     if not torch.cuda.is_available():
         print("microbench needs a GPU", file=sys.stderr)
         sys.exit(1)
-    props, rows, per_cu = run(args.quick)
+    props, rows, per_cu = run(args.quick, args.only.split(",") if args.only else None)
     lines = ["# gfx950 microbenchmarks", "",
              "Command: `python -m microbench.run%s`" % (" --quick" if args.quick else ""), "",
              "Device: %s, %d compute units; one work-group per compute unit; figures in shader "
