@@ -3,11 +3,18 @@
     python bench_profiles.py trace    --dir D --kernel SUB --bench-log L --cmd C --title T --out F
     python bench_profiles.py counters --sq D1 --fetch D2 --write D3 --kernel SUB --workload W
                                       --dtype bf16|fp8 --key K --cmds F --title T --out F
+    python bench_profiles.py traffic  --fetch D2 --write D3 --kernel SUB --key K --dtype quant
+                                      --steps-total S --cmds F --title T --out F [--note F]
+    python bench_profiles.py mix      --sq D1 --kernel SUB --dtype bwd --cmds F --title T --out F
 
 ``trace`` reads the ``*_kernel_stats.csv`` of a ``rocprofv3 --kernel-trace
 --stats --output-format csv`` run and the bench JSON line the same run
 printed, and writes the kernel's calls and average / min / max duration next
 to bench.py's own HIP-event figures.
+
+``mix`` reads one SQ run and tabulates each matching kernel (the backward
+pass's three).  ``traffic`` reads only the FETCH_SIZE and WRITE_SIZE runs (for the HBM-bound
+quantiser) and reports them per kernel and per step.
 
 ``counters`` reads three ``rocprofv3 --pmc`` runs (the SQ instruction and
 busy counters with GRBM_GUI_ACTIVE; FETCH_SIZE; WRITE_SIZE, the last two
@@ -88,20 +95,23 @@ def _copy_counter(per, name):
 
 def cmd_trace(a):
     rows, total = kernel_stats(a.dir)
-    b = bench_line(a.bench_log)
     out = ["# " + a.title, "", "Command (from the repository root, library built):", "", "```",
            a.cmd, "```", "", "| kernel | calls | average µs | min µs | max µs |",
            "|---|---|---|---|---|"]
-    share, kavg = 0.0, None
+    # GPU time per step: each matching kernel's average times its launches
+    # per step (its calls over the run's warm-up and timed steps)
+    b = bench_line(a.bench_log)
+    nsteps = b["steps"] + b["warmup"]
+    share, kavg, nmatch = 0.0, 0.0, 0
     for r in rows:
         if a.kernel in r["Name"]:
             out.append("| `%s` | %s | %.1f | %.1f | %.1f |" % (
                 r["Name"], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
                 float(r["MaxNs"]) / 1e3))
             share += float(r["TotalDurationNs"])
-            if kavg is None:
-                kavg = float(r["AverageNs"]) / 1e3
-    if kavg is None:
+            kavg += float(r["AverageNs"]) / 1e3 * round(float(r["Calls"]) / nsteps)
+            nmatch += 1
+    if not nmatch:
         raise SystemExit("no kernel matches %r" % a.kernel)
     rf = b["roofline"]
     out += ["", "Matching kernels: %.2f%% of all GPU time in the run (the rest is input upload "
@@ -110,8 +120,10 @@ def cmd_trace(a):
             "The same run's bench line, with HIP events on the launch stream over the %d timed "
             "launches:" % b["steps"], ""]
     if "kernel_avg_ms" in rf:
-        out.append("- average launch %.1f µs (profiler average above: %.1f µs, ratio %.3f)" % (
-            rf["kernel_avg_ms"] * 1e3, kavg, rf["kernel_avg_ms"] * 1e3 / kavg))
+        what = ("profiler average above" if nmatch == 1 else
+                "the %d kernels' profiler averages above times their launches per step" % nmatch)
+        out.append("- average step %.1f µs (%s: %.1f µs, ratio %.3f)" % (
+            rf["kernel_avg_ms"] * 1e3, what, kavg, rf["kernel_avg_ms"] * 1e3 / kavg))
     out.append("- %.1f %s per launch = %.3f of the peak (%.1f %s)" % (
         rf["achieved"], rf["unit"], rf["frac"], rf["peak"], rf["unit"]))
     out.append("- whole-run value %.1f %s, %.4f ms per step" % (b["value"], b["unit"],
@@ -217,6 +229,78 @@ def cmd_counters(a):
     print("wrote", a.out, "hbm", hbm, "busy %.3f valu/mfma %.2f clock %.0f" % (busy, vpm, clock))
 
 
+def cmd_traffic(a):
+    """HBM traffic only (FETCH_SIZE and WRITE_SIZE runs, no SQ run): per
+    kernel per dispatch, and per step for a multi-launch entry point."""
+    import bench
+    fe, _ = counter_rows(a.fetch)
+    wr, _ = counter_rows(a.write)
+    cf, cw = _copy_counter(fe, "FETCH_SIZE"), _copy_counter(wr, "WRITE_SIZE")
+    ff, fw = 1048576.0 / cf, 1048576.0 / cw
+    rows, tf, tw = [], 0.0, 0.0
+    for name in sorted(k for k in fe if a.kernel in k):
+        f = sum(fe[name]["FETCH_SIZE"]) / len(fe[name]["FETCH_SIZE"])
+        w = sum(wr[name]["WRITE_SIZE"]) / len(wr[name]["WRITE_SIZE"])
+        per_step = round(len(fe[name]["FETCH_SIZE"]) / a.steps_total)
+        rows.append((name, f, w, per_step))
+        tf += f * per_step
+        tw += w * per_step
+    if not rows:
+        raise SystemExit("no kernel matches %r" % a.kernel)
+    hbm = int(round((tf * ff + tw * fw) * 1024))
+    src = bench.kernel_source_hash(a.dtype)
+    cmds = [l.rstrip("\n") for l in open(a.cmds) if l.strip()]
+    out = ["# " + a.title, "", "Two runs, one counter each (never combined with traces other "
+           "than the kernel trace):", "", "```"] + cmds + ["```", ""]
+    if a.note:
+        out += [open(a.note).read().strip(), ""]
+    out += ["The 1 GiB device copy after the timed region calibrates the counters: FETCH_SIZE "
+            "reads %.0f KiB for it (scale factor %.4f), WRITE_SIZE %.0f KiB (%.4f)." % (
+                cf, ff, cw, fw), "",
+            "| kernel | launches per step | FETCH_SIZE KiB per launch | WRITE_SIZE KiB per launch |",
+            "|---|---|---|---|"]
+    for name, f, w, n in rows:
+        out.append("| `%s` | %d | %.1f | %.1f |" % (name, n, f, w))
+    out += ["", "Per step, scaled: %.1f MiB fetched + %.1f MiB written = %.1f MiB." % (
+        tf * ff / 1024, tw * fw / 1024, hbm / 2 ** 20), "",
+            "Kernel source hash (bench.py `kernel_source_hash('%s')`): `%s`" % (a.dtype, src)]
+    with open(a.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+    _update(TRAFFIC_FILE, a.key, [src, "%.1f" % tf, "%.5f" % ff, "%.1f" % tw, "%.5f" % fw, hbm],
+            ["# key kernel_source_hash fetch_KiB fetch_factor write_KiB write_factor hbm_bytes"])
+    print("wrote", a.out, "hbm", hbm)
+
+
+def cmd_mix(a):
+    """SQ instruction mix only (one run), kernel by kernel: for a
+    multi-kernel entry point such as the backward pass."""
+    import bench
+    sq, sq_dur = counter_rows(a.sq)
+    cmds = [l.rstrip("\n") for l in open(a.cmds) if l.strip()]
+    out = ["# " + a.title, "", "One run of the SQ counter group (never combined with traces "
+           "other than the kernel trace):", "", "```"] + cmds + ["```", "",
+           "| kernel | µs under counters | MHz | matrix cores busy | VALU per MFMA | "
+           "LDS per MFMA | LDS bank conflicts |", "|---|---|---|---|---|---|---|"]
+    for name in sorted(k for k in sq if a.kernel in k):
+        v = {c: sum(sq[name][c]) / len(sq[name][c]) for c in SQ}
+        dur = sum(sq_dur[name]) / len(sq_dur[name])
+        cyc = v["GRBM_GUI_ACTIVE"] / XCDS
+        mf = v["SQ_INSTS_MFMA"]
+        per = (lambda x: "%.2f" % (x / mf)) if mf > 0 else (lambda x: "-")
+        out.append("| `%s` | %.1f | %.0f | %.3f | %s | %s | %.3g |" % (
+            name, dur / 1e3, cyc / dur * 1e3, v["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc),
+            per(v["SQ_INSTS_VALU"] - mf), per(v["SQ_INSTS_LDS"]), v["SQ_LDS_BANK_CONFLICT"]))
+    out += ["", "Matrix cores busy: SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x GRBM_GUI_ACTIVE "
+            "per XCD); VALU per MFMA excludes the MFMAs (SQ_INSTS_VALU counts them); the clock "
+            "is GRBM_GUI_ACTIVE per XCD over the kernel's duration (a lower bound, and meaningless "
+            "for a kernel as short as the counter window's overhead)." % SIMDS, "",
+            "Kernel source hash (bench.py `kernel_source_hash('%s')`): `%s`" % (
+                a.dtype, bench.kernel_source_hash(a.dtype))]
+    with open(a.out, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("wrote", a.out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -235,8 +319,19 @@ def main():
                         "--workload and --bench-args)")
     c.add_argument("--bench-args", default="", help="extra bench.py arguments of the runs")
     c.add_argument("--dtype", required=True, choices=["bf16", "fp8", "quant", "bwd"])
+    r = sub.add_parser("traffic")
+    for n in ("--fetch", "--write", "--kernel", "--key", "--title", "--out", "--cmds"):
+        r.add_argument(n, required=True)
+    r.add_argument("--steps-total", type=int, required=True,
+                   help="warm-up plus timed steps of the counter runs")
+    r.add_argument("--note", default=None, help="file with a paragraph for the summary")
+    r.add_argument("--dtype", required=True, choices=["bf16", "fp8", "quant", "bwd"])
+    m = sub.add_parser("mix")
+    for n in ("--sq", "--kernel", "--title", "--out", "--cmds"):
+        m.add_argument(n, required=True)
+    m.add_argument("--dtype", required=True, choices=["bf16", "fp8", "quant", "bwd"])
     a = ap.parse_args()
-    (cmd_trace if a.what == "trace" else cmd_counters)(a)
+    {"trace": cmd_trace, "counters": cmd_counters, "traffic": cmd_traffic, "mix": cmd_mix}[a.what](a)
 
 
 if __name__ == "__main__":
