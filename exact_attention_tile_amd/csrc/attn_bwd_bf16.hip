@@ -728,14 +728,18 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 //   phase 2i+3:  P wave  P(i+1)          (vector ALU)    | dS wave  dK(i), dP(i+1)
 // (phase 0: S(0) | dP(0); phase 1: P(0) | -), so one wave of a SIMD issues
 // products while the other issues its vector work.  S and dP are computed
-// once per (query, key) pair.  Tile i is read in phases 2i .. 2i+3, so the Q
-// and dO tiles rotate through three LDS buffers: tile k+1 is loaded (Q by
-// the P waves, dO by the dS waves, lse by wave 0, D by wave 4) at the start
-// of phase 2k and waited for at the end of phase 2k+1.  The accumulation
-// order per key is the tiles', then 16-query groups, so the results do not
-// depend on the split.  Operands are read from LDS four products ahead; the
-// swizzled offsets of k-step ks and column block db are the first ones XOR
-// 16 ks and XOR 32 db (elements).
+// once per (query, key) pair.  Q tile i is read in phases 2i .. 2i+3 and dO
+// tile i in phases 2i+1 and 2i+2, so Q tiles rotate through three LDS
+// buffers and dO tiles through two.  Each wave issues its share of the next
+// tile's loads at the start of its vector phase, where they delay neither
+// wave's products: the dS waves load Q and lse (tile k+1 in phase 2k), the
+// P waves dO and D (tile k+1 in phase 2k+1); each waits for its own loads
+// at the end of the following phase.  The accumulation order per key is the
+// tiles', then 16-query groups, so the results do not depend on the split.
+// A matrix-core phase is one stream of 32 products whose operands are read
+// from LDS four products ahead, the first four at the end of the vector
+// phase before it; the swizzled offsets of k-step ks and column block db are
+// the first ones XOR 16 ks and XOR 32 db (elements).
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p) {
@@ -777,17 +781,20 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
   const int nt = n_q_all - first;                          // >= 1: k0 < N
   const int n_phases = 2 * nt + 2;
 
-  // this wave's share of the tile loads: Q and lse (P waves; tile k+1 at
-  // the start of phase 2k, waited for at the end of phase 2k+1) or dO and D
-  // (dS waves; tile k+1 at the start of phase 2k+1, waited for at the end of
-  // phase 2k+2).  Q tile i is read in phases 2i .. 2i+3, dO tile i in phases
-  // 2i+1 and 2i+2, hence three Q buffers and two dO buffers.
-  const __bf16* __restrict__ src = (const __bf16*)(role ? p.dout : p.q) + head_base;
-  const float* __restrict__ rsrc = (role ? p.delta : p.lse) + (long long)bh * N;
+  // this wave's share of the tile loads, issued in its vector phases (the
+  // matrix-core phase of its partner wave, which they would otherwise
+  // delay): Q and lse (dS waves, lr = 0; tile k+1 at the start of phase 2k,
+  // waited for at the end of phase 2k+1) or dO and D (P waves, lr = 1; tile
+  // k+1 at the start of phase 2k+1, waited for at the end of phase 2k+2).
+  // Q tile i is read in phases 2i .. 2i+3, dO tile i in phases 2i+1 and
+  // 2i+2, hence three Q buffers and two dO buffers.
+  const int lr = 1 - role;
+  const __bf16* __restrict__ src = (const __bf16*)(lr ? p.dout : p.q) + head_base;
+  const float* __restrict__ rsrc = (lr ? p.delta : p.lse) + (long long)bh * N;
   TileLoader<D, KW, BQ> ld;
   ld.init(kgrp, lane, tok);
-  const unsigned lds_dst = (unsigned)(size_t)((ATTN_LDS __bf16*)(role ? gsm : qsm));
-  const int nbuf = role ? 2 : NB;
+  const unsigned lds_dst = (unsigned)(size_t)((ATTN_LDS __bf16*)(lr ? gsm : qsm));
+  const int nbuf = lr ? 2 : NB;
   float row_val = 0.f;
   auto load_tile = [&](int u) {
     const int q0t = (first + u) * BQ;
@@ -795,20 +802,35 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
     if (kgrp == 0) row_val = rsrc[min(q0t + lane, N - 1)];
   };
   auto store_rowv = [&](int u) {
-    if (kgrp == 0) rowv[u % NB][role][lane] = role ? row_val : row_val * kLog2e;
+    if (kgrp == 0) rowv[u % NB][lr][lane] = lr ? row_val : row_val * kLog2e;
   };
   // the tile loads and barriers every wave takes part in, around phase ph
   auto phase_begin = [&](int ph) {
-    const int k = (ph - role) >> 1;
-    if (((ph - role) & 1) == 0 && ph >= role && k + 1 < nt) load_tile(k + 1);
+    const int k = (ph - lr) >> 1;
+    if (((ph - lr) & 1) == 0 && ph >= lr && k + 1 < nt) load_tile(k + 1);
   };
   auto phase_end = [&](int ph) {
-    const int k = (ph - 1 - role) >> 1;
-    if (((ph - 1 - role) & 1) == 0 && ph >= 1 + role) {
+    const int k = (ph - 1 - lr) >> 1;
+    if (((ph - 1 - lr) & 1) == 0 && ph >= 1 + lr) {
       wait_vmem();
       if (k + 1 < nt) store_rowv(k + 1);
     }
     __syncthreads();
+  };
+  // the end of a vector phase that read the next phase's first PF operands
+  // (2 PF LDS reads, issued last): the barrier waits for this wave's earlier
+  // LDS accesses, whose writes the other waves read next, but not for those
+  // reads (LDS accesses complete in order).  No tile load is awaited at the
+  // end of a vector phase; the general form is kept for that case.
+  auto phase_end_pre = [&](int ph) {
+    const int k = (ph - 1 - lr) >> 1;
+    if (((ph - 1 - lr) & 1) == 0 && ph >= 1 + lr) {
+      wait_vmem();
+      if (k + 1 < nt) store_rowv(k + 1);
+      __syncthreads();
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(2 * PF) : "memory");
+    }
   };
 
   // element offsets: row reads (k-step 0) and transposing reads (column
@@ -839,83 +861,113 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
   }
   __syncthreads();
 
-  // S (P wave) or dP (dS wave) of tile u: 2 blocks of 32 queries, A = the
-  // tile's Q or dO rows, B = this wave's K or V rows
-  f32x16 acc2[2];
-  auto score = [&](auto role_tag, int u) __attribute__((always_inline)) {
-    constexpr int R = decltype(role_tag)::value;
-    int eb = (u % (R ? 2 : NB)) * TILE;
-    int qo = qoff0;
-    asm volatile("" : "+s"(eb), "+v"(qo));
-    const __bf16* t = (R ? gsm : qsm) + eb;
-    const __bf16* vt = vsm + kgrp * 32 * D;
-    constexpr int NP = 2 * NKS;           // products (ks, qb), ks-major
-    bf16x8 a[NP], vb[NKS];
-    auto rd = [&](int i) __attribute__((always_inline)) {
-      const int ks = i >> 1, qb = i & 1;
-      a[i] = *(const bf16x8*)(t + qb * 32 * D + (qo ^ (16 * ks)));
-      if constexpr (R == 1)
-        if (qb == 0) vb[ks] = *(const bf16x8*)(vt + (qo ^ (16 * ks)));
-    };
-#pragma unroll
-    for (int i = 0; i < PF; ++i) rd(i);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      if (i + PF < NP) rd(i + PF);
-      const int ks = i >> 1, qb = i & 1;
-      const bf16x8 bop = R ? vb[ks] : bf[ks];
-      acc2[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bop, ks == 0 ? f32x16{} : acc2[qb], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave) for tile u: A = the
-  // tile's dO or Q rows, transposed; B = the packed P or dS
-  f32x16 acc[NDB];
+  f32x16 acc2[2];                         // S (P wave) or dP (dS wave) of a tile
+  f32x16 acc[NDB];                        // dV^T (P wave) or dK^T (dS wave)
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   bf16x8 pk[2][2];                        // [qb][g]: P or dS, packed
-  auto update = [&](auto role_tag, int u) __attribute__((always_inline)) {
+  // One matrix-core phase as one stream of products, whose LDS operands are
+  // read PF products ahead across the join of its two parts:
+  //   the update of tile uu: dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS
+  //   wave); A = the tile's dO or Q rows, transposed; B = the packed P or dS;
+  //   the scores of tile us: S = Q K^T (P wave) or dP = dO V^T (dS wave), 2
+  //   blocks of 32 queries; A = the tile's Q or dO rows, B = this wave's K
+  //   or V rows.
+  // The first phase has no update and the last no scores.  With PRE the
+  // first PF operands were read at the end of the vector phase before
+  // (pre_read), so the first product does not wait for LDS after the barrier.
+  bf16x8 apre[PF];
+  auto upd_operand = [&](const __bf16* tu, int lo, int hi, int i) __attribute__((always_inline)) {
+    const int qb = i / (2 * NDB), g = (i / NDB) & 1, db = i % NDB;
+    return tr_operand(tu + (32 * qb + 16 * g) * D, lo ^ (32 * db), hi ^ (32 * db));
+  };
+  auto upd_tile = [&](auto role_tag, int uu, int& lo, int& hi) __attribute__((always_inline)) {
     constexpr int R = decltype(role_tag)::value;
-    int eb = (u % (R ? NB : 2)) * TILE;
-    int lo = tro.lo[0], hi = tro.hi[0];
+    int eb = (uu % (R ? NB : 2)) * TILE;
+    lo = tro.lo[0];
+    hi = tro.hi[0];
     asm volatile("" : "+s"(eb), "+v"(lo), "+v"(hi));
-    const __bf16* t = (R ? qsm : gsm) + eb;
-    constexpr int NP = 4 * NDB;           // products (qb, g, db)
-    bf16x8 a[NP];
+    return (R ? qsm : gsm) + eb;
+  };
+  auto pre_read = [&](auto role_tag, int uu) __attribute__((always_inline)) {
+    int lo, hi;
+    const __bf16* tu = upd_tile(role_tag, uu, lo, hi);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) apre[i] = upd_operand(tu, lo, hi, i);
+  };
+  auto xphase = [&](auto role_tag, auto upd_tag, auto sc_tag, auto pre_tag, int uu, int us)
+      __attribute__((always_inline)) {
+    constexpr int R = decltype(role_tag)::value;
+    constexpr bool UPD = decltype(upd_tag)::value, SC = decltype(sc_tag)::value;
+    constexpr bool PRE = decltype(pre_tag)::value;
+    constexpr int NU = UPD ? 4 * NDB : 0;   // update products (qb, g, db)
+    constexpr int NP = NU + (SC ? 2 * NKS : 0);   // then score products (ks, qb), ks-major
+    static_assert(!PRE || NU >= PF, "pre-read operands are update operands");
+    int lo = 0, hi = 0;
+    const __bf16* tu = UPD ? upd_tile(role_tag, uu, lo, hi) : qsm;
+    int eb = (us % (R ? 2 : NB)) * TILE;
+    int qo = qoff0;
+    asm volatile("" : "+s"(eb), "+v"(qo));
+    const __bf16* ts = (R ? gsm : qsm) + eb;
+    const __bf16* vt = vsm + kgrp * 32 * D;
+    bf16x8 a[NP], vb[NKS];
     auto rd = [&](int i) __attribute__((always_inline)) {
-      const int qb = i / (2 * NDB), g = (i / NDB) & 1, db = i % NDB;
-      a[i] = tr_operand(t + (32 * qb + 16 * g) * D, lo ^ (32 * db), hi ^ (32 * db));
+      if (i < NU) {
+        a[i] = upd_operand(tu, lo, hi, i);
+      } else {
+        const int ks = (i - NU) >> 1, qb = (i - NU) & 1;
+        a[i] = *(const bf16x8*)(ts + qb * 32 * D + (qo ^ (16 * ks)));
+        if constexpr (R == 1)
+          if (qb == 0) vb[ks] = *(const bf16x8*)(vt + (qo ^ (16 * ks)));
+      }
     };
 #pragma unroll
-    for (int i = 0; i < PF; ++i) rd(i);
+    for (int i = 0; i < PF; ++i) {
+      if constexpr (PRE)
+        a[i] = apre[i];
+      else
+        rd(i);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
       if (i + PF < NP) rd(i + PF);
-      const int qb = i / (2 * NDB), g = (i / NDB) & 1, db = i % NDB;
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], pk[qb][g], acc[db], 0, 0, 0);
+      if (i < NU) {
+        const int qb = i / (2 * NDB), g = (i / NDB) & 1, db = i % NDB;
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], pk[qb][g], acc[db], 0, 0, 0);
+      } else {
+        const int ks = (i - NU) >> 1, qb = (i - NU) & 1;
+        const bf16x8 bop = R ? vb[ks] : bf[ks];
+        acc2[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bop, ks == 0 ? f32x16{} : acc2[qb], 0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
+  // The packed values are computed in the vector phase: without this the
+  // compiler sinks their arithmetic past the barrier into the wave's
+  // matrix-core phase, where it cannot overlap the wave's own products.
+  auto pin_packed = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(pk[0][0]), "+v"(pk[0][1]), "+v"(pk[1][0]), "+v"(pk[1][1]));
+  };
   // register r of block qb holds query q0t + 32 qb + 8 (r/4) + 4 lh + r%4 of
   // key mykey; quarter x = r/4 = 2 g + half.  The vector phases go group by
-  // group (qb, g), the LDS values of the next group read one group ahead.
+  // group (qb, g); the P wave reads all its lse values first, the dS wave
+  // reads each group's LDS values one group ahead.
   auto p_values = [&](auto masked_tag, int u) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int buf = u % NB;
     const int q0t = (first + u) * BQ;
+    // every group's lse is read up front: the partner wave's operand reads
+    // keep the LDS queue long, and a read one group ahead stalls each group
     f32x4 lv[4][2];                       // [group][half]
-    auto rd = [&](int gi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
       for (int half = 0; half < 2; ++half)
         lv[gi][half] = *(const f32x4*)&rowv[buf][0][16 * gi + 8 * half + 4 * lh];
-    };
-    rd(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {      // gi = 2 qb + g
-      if (gi + 1 < 4) rd(gi + 1);
       const int qb = gi >> 1, g = gi & 1;
       u32x4 w;
 #pragma unroll
@@ -938,6 +990,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
       pk[qb][g] = __builtin_bit_cast(bf16x8, w);
       __builtin_amdgcn_sched_barrier(0);
     }
+    pin_packed();
   };
   auto ds_values = [&](int u) __attribute__((always_inline)) {
     const int buf = u % NB;
@@ -970,6 +1023,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
       pk[qb][g] = __builtin_bit_cast(bf16x8, w);
       __builtin_amdgcn_sched_barrier(0);
     }
+    pin_packed();
   };
   // tile u's P needs the mask: causal diagonal (or keys after all its
   // queries) or rows past N
@@ -983,12 +1037,15 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
   using R0 = std::integral_constant<int, 0>;
   using R1 = std::integral_constant<int, 1>;
   // Each loop iteration is one (matrix-core, vector) phase pair, so the
-  // accumulators keep their registers from phase to phase.
+  // accumulators keep their registers from phase to phase.  A vector phase
+  // ends by reading the first operands of the wave's next update (its tile
+  // is complete: it was awaited before the barrier that began the phase);
+  // an empty asm keeps those reads after the phase's LDS writes.
   if (role == 0) {
     // phase 0: S(0); phase 1: P(0); phase 2i+2: dV(i), S(i+1); phase 2i+3: P(i+1)
     phase_begin(0);
     __builtin_amdgcn_s_setprio(3);
-    score(R0{}, 0);
+    xphase(R0{}, F_{}, T_{}, F_{}, 0, 0);
     __builtin_amdgcn_s_setprio(0);
     phase_end(0);
     phase_begin(1);
@@ -996,12 +1053,13 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
       p_values(T_{}, 0);
     else
       p_values(F_{}, 0);
-    phase_end(1);
+    asm volatile("" ::: "memory");
+    pre_read(R0{}, 0);
+    phase_end_pre(1);
     for (int i = 0; i + 1 < nt; ++i) {
       phase_begin(2 * i + 2);
       __builtin_amdgcn_s_setprio(3);
-      update(R0{}, i);
-      score(R0{}, i + 1);
+      xphase(R0{}, T_{}, T_{}, T_{}, i, i + 1);
       __builtin_amdgcn_s_setprio(0);
       phase_end(2 * i + 2);
       phase_begin(2 * i + 3);
@@ -1009,10 +1067,12 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
         p_values(T_{}, i + 1);
       else
         p_values(F_{}, i + 1);
-      phase_end(2 * i + 3);
+      asm volatile("" ::: "memory");
+      pre_read(R0{}, i + 1);
+      phase_end_pre(2 * i + 3);
     }
     phase_begin(2 * nt);
-    update(R0{}, nt - 1);
+    xphase(R0{}, T_{}, F_{}, T_{}, nt - 1, 0);
     phase_end(2 * nt);
     phase_begin(2 * nt + 1);
     phase_end(2 * nt + 1);
@@ -1020,7 +1080,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
     // phase 0: dP(0); phase 1: -; phase 2i+2: dS(i); phase 2i+3: dK(i), dP(i+1)
     phase_begin(0);
     __builtin_amdgcn_s_setprio(3);
-    score(R1{}, 0);
+    xphase(R1{}, F_{}, T_{}, F_{}, 0, 0);
     __builtin_amdgcn_s_setprio(0);
     phase_end(0);
     phase_begin(1);
@@ -1028,19 +1088,22 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
     for (int i = 0; i + 1 < nt; ++i) {
       phase_begin(2 * i + 2);
       ds_values(i);
-      phase_end(2 * i + 2);
+      asm volatile("" ::: "memory");
+      pre_read(R1{}, i);
+      phase_end_pre(2 * i + 2);
       phase_begin(2 * i + 3);
       __builtin_amdgcn_s_setprio(3);
-      update(R1{}, i);
-      score(R1{}, i + 1);
+      xphase(R1{}, T_{}, T_{}, T_{}, i, i + 1);
       __builtin_amdgcn_s_setprio(0);
       phase_end(2 * i + 3);
     }
     phase_begin(2 * nt);
     ds_values(nt - 1);
-    phase_end(2 * nt);
+    asm volatile("" ::: "memory");
+    pre_read(R1{}, nt - 1);
+    phase_end_pre(2 * nt);
     phase_begin(2 * nt + 1);
-    update(R1{}, nt - 1);
+    xphase(R1{}, T_{}, F_{}, T_{}, nt - 1, 0);
     phase_end(2 * nt + 1);
   }
 
