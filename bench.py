@@ -168,6 +168,14 @@ def algorithmic_bytes(w):
     return T * w.d * (w.H * e + 2 * w.kv_heads * e + w.H * 2) + T * w.H * 4
 
 
+def algorithmic_bytes_bwd(w):
+    """HBM bytes one backward call must move: q, k, v, o and dO read once,
+    dQ, dK and dV written once (bf16), lse read once, and the fp32 D
+    workspace written once and read once."""
+    T = w.total
+    return T * w.d * 2 * (4 * w.H + 4 * w.kv_heads) + T * w.H * 4 * 3
+
+
 def secondary_roofs(w, flops, achieved, ctr, mb):
     """The two on-chip roofs beside the matrix-core peak, in TFLOP/s of the
     metric's flops (each at the nominal 2.4 GHz, like the peak):
@@ -573,6 +581,13 @@ def main():
     if args.which in ("bwd", "fwd2"):
         out["config"]["pass"] = args.which
         rf["traffic"] = None
+    if args.which == "bwd":
+        # per call (the three kernels), like achieved
+        rf["traffic"] = measured_traffic(w.name, "bwd", causal,
+                                         key="%s_bwd%s" % (w.name, "" if causal else "_noncausal"))
+        rf["algorithmic_bytes"] = algorithmic_bytes_bwd(w)
+        rf["traffic_ratio"] = (round(rf["traffic"] / rf["algorithmic_bytes"], 3)
+                               if rf["traffic"] else None)
     if args.which == "fwd2":
         out["metric"] = METRIC_FWD2
     if not args.no_cpu_baseline and args.which in ("fwd", "fwd2"):

@@ -61,9 +61,10 @@ def load():
     lib.mb_tile_loads.argtypes = [i, i, i, i, i, vp, ctypes.c_longlong, vp, vp, vp]
     lib.mb_mfma_chain.argtypes = [i, i, i, i, vp, vp, vp]
     lib.mb_lds_latency.argtypes = [i, i, i, vp, vp, vp]
+    lib.mb_dq_atomics.argtypes = [i, i, i, vp, ctypes.c_float, vp]
     for f in (lib.mb_valu_rate, lib.mb_mfma_pair, lib.mb_lds_read, lib.mb_mfma_lds,
               lib.mb_mfma_one, lib.mb_mfma_inwave, lib.mb_tile_loads, lib.mb_mfma_chain,
-              lib.mb_lds_latency):
+              lib.mb_lds_latency, lib.mb_dq_atomics):
         f.restype = i
     _LIB = lib
     return lib

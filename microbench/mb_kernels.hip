@@ -678,6 +678,42 @@ __global__ __launch_bounds__(256, 1) void lds_latency(Stamp* out, float* sink, i
   stamp_store(out, blockDim.x >> 6, c0, c1, r0, r1);
   sink[blockIdx.x * blockDim.x + threadIdx.x] = (float)addr;
 }
+
+// ---------------------------------------------------------------------------
+// dQ accumulated with fp32 atomics, the traffic pattern of a causal backward
+// that would add each key tile's dQ contribution into a shared fp32 buffer:
+// work-group (bh, kt) of 256 threads adds a 64 x 128 fp32 tile into rows
+// [64 qt, 64 qt + 64) of head bh for every 64-query tile qt >= 2 kt (the
+// queries that see its 128 keys).  Wave w covers columns 32 w .. 32 w + 31;
+// register r of block qb is row 32 qb + 8 (r/4) + 4 lh + r%4 (the MFMA
+// accumulator layout), value (r + 1) * v.  MODE 0: agent-scope atomic add
+// without return; 1: plain stores of the same addresses (the bandwidth
+// reference).  Work-group L adds into head L % bh_n, so with bh_n a multiple
+// of 8 all of a head's tiles run on one XCD and share its L2.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void dq_atomics(float* __restrict__ acc, int bh_n, int n, float v) {
+  const int kt_n = n / 128, nq = n / 64;
+  const int bh = blockIdx.x % bh_n, kt = blockIdx.x / bh_n;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ln = lane & 31, lh = lane >> 5;
+  (void)kt_n;
+  float* base = acc + (long long)bh * n * 128 + 32 * wave + ln;
+  for (int qt = 2 * kt; qt < nq; ++qt) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = qt * 64 + 32 * qb + 8 * (r >> 2) + 4 * lh + (r & 3);
+        float* a = base + (long long)row * 128;
+        const float x = v * (float)(r + 1);
+        if constexpr (MODE == 0)
+          __hip_atomic_fetch_add(a, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          *a = x;
+      }
+  }
+}
 }  // namespace mb
 
 // ---------------------------------------------------------------------------
@@ -789,5 +825,14 @@ extern "C" int mb_lds_latency(int kind, int grid, int iters, void* stamps, float
   mb::Stamp* st = (mb::Stamp*)stamps;
   if (kind == 0) return (int)mb::launch(mb::lds_latency<0>, grid, 256, s, st, sink, iters);
   if (kind == 1) return (int)mb::launch(mb::lds_latency<1>, grid, 256, s, st, sink, iters);
+  return (int)hipErrorInvalidValue;
+}
+
+// acc: bh_n * n * 128 floats on the device; n a multiple of 128
+extern "C" int mb_dq_atomics(int mode, int bh_n, int n, float* acc, float v, hipStream_t s) {
+  if (bh_n < 1 || n < 128 || n % 128 != 0 || acc == nullptr) return (int)hipErrorInvalidValue;
+  const int grid = bh_n * (n / 128);
+  if (mode == 0) return (int)mb::launch(mb::dq_atomics<0>, grid, 256, s, acc, bh_n, n, v);
+  if (mode == 1) return (int)mb::launch(mb::dq_atomics<1>, grid, 256, s, acc, bh_n, n, v);
   return (int)hipErrorInvalidValue;
 }

@@ -22,7 +22,10 @@ Rows:
   lds       LDS bytes read per cycle per compute unit (ds_read_b128,
             ds_read_b64, ds_read_b64_tr_b16) with 4, 8 or 16 waves;
   mfma+lds  cycles per MFMA when its A operand is a 1 KiB ds_read_b128
-            fragment, as in the attention kernels' matrix-core phase.
+            fragment, as in the attention kernels' matrix-core phase;
+  atomics   fp32 atomic adds in the pattern a backward pass would need to
+            accumulate dQ across key tiles (long8k's 32 heads, N = 8192,
+            d = 128), against plain stores of the same addresses.
 """
 
 import argparse
@@ -119,6 +122,35 @@ class Runner:
         self._launch(self.lib.mb_lds_latency, kind, self.grid, iters)
         return self._read(4)
 
+    def dq_atomics(self, bh, n, reps):
+        """ms per launch of the atomic and the plain-store form, and the
+        number of elements whose atomic sum (one launch from zero) differs
+        from the exact value."""
+        torch = self.torch
+        acc = torch.zeros(bh * n * 128, dtype=torch.float32, device="cuda")
+        out = {}
+        for mode in (1, 0):
+            for _ in range(2):
+                if self.lib.mb_dq_atomics(mode, bh, n, acc.data_ptr(), 1.0, self.stream) != 0:
+                    raise RuntimeError("mb_dq_atomics failed")
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                self.lib.mb_dq_atomics(mode, bh, n, acc.data_ptr(), 1.0, self.stream)
+            b.record()
+            torch.cuda.synchronize()
+            out[mode] = a.elapsed_time(b) / reps
+        acc.zero_()
+        if self.lib.mb_dq_atomics(0, bh, n, acc.data_ptr(), 1.0, self.stream) != 0:
+            raise RuntimeError("mb_dq_atomics failed")
+        torch.cuda.synchronize()
+        got = acc.view(bh, n, 128).cpu().numpy()
+        row = np.arange(n)
+        x = row % 32
+        want = ((row // 64) // 2 + 1) * (4 * (x // 8) + x % 4 + 1)
+        bad = int((got != want[None, :, None].astype(np.float32)).sum())
+        return out[0], out[1], bad
+
 
 def _mhz(cyc, rt):
     ok = rt > 0
@@ -131,7 +163,7 @@ VALU_OPS = [(0, "v_fma_f32", 16), (1, "v_exp_f32", 16), (2, "v_add_f32", 16),
 
 
 def run(quick=False, only=None):
-    """All rows, or (only = list of "chain", "ldslat") just those groups."""
+    """All rows, or (only = list of "chain", "ldslat", "atomics") just those groups."""
     import torch
 
     def want(name):
@@ -161,6 +193,20 @@ def run(quick=False, only=None):
             rows.append(("lds latency", name, "1 wave/SIMD, dependent reads",
                          "%.1f cycles per read" % (np.median(cyc) / (iters * 16)),
                          _mhz(cyc, rt)))
+    # fp32 atomics in the pattern of a causal backward accumulating dQ (32 heads,
+    # N = 8192, d = 128: every 128-key tile adds into the rows of the queries it sees)
+    if want("atomics"):
+        bh, n = 32, 8192
+        tiles = bh * sum(n // 64 - 2 * kt for kt in range(n // 128))
+        gb = tiles * 64 * 128 * 4 / 1e9
+        t_at, t_st, bad = r.dq_atomics(bh, n, 3 if quick else 5)
+        rows.append(("atomics", "global_atomic_add_f32 (agent scope, no return), "
+                     "%.2f GB of fp32 adds" % gb, "4 waves per work-group, %d work-groups" % (
+                         bh * n // 128),
+                     "%.3f ms = %.0f GB/s (plain stores of the same addresses: %.3f ms = %.0f "
+                     "GB/s); exact sums, %d elements differ" % (t_at, gb / t_at * 1e3, t_st,
+                                                               gb / t_st * 1e3, bad),
+                     float("nan")))
     if only:
         return props, rows, r.max_per_cu
 
@@ -254,7 +300,7 @@ def main():
     ap.add_argument("--out", default=None)
     ap.add_argument("--quick", action="store_true", help="a quarter of the iterations")
     ap.add_argument("--only", default=None,
-                    help="comma-separated groups to run alone: chain, ldslat")
+                    help="comma-separated groups to run alone: chain, ldslat, atomics")
     args = ap.parse_args()
     import torch
     if not torch.cuda.is_available():
