@@ -10,6 +10,8 @@
 #include "attn.h"
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <math.h>
 #include <stdint.h>
 
@@ -66,6 +68,23 @@ int validate_fixed(int B, int N, int64_t* tokens) {
   return ATTN_OK;
 }
 
+// Compute units of the current device, read once per device (0 when it
+// cannot be read: then every launch has one work-group per item).
+int device_compute_units() {
+  static std::atomic<int> known[64];   // 0: not read yet, -1: unavailable
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = known[dev].load(std::memory_order_relaxed);
+    if (v != 0) return v > 0 ? v : 0;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = -1;
+  if (dev < 64) known[dev].store(n, std::memory_order_relaxed);
+  return n > 0 ? n : 0;
+}
+
 int validate_descales(const float* dq, const float* dk, const float* dv) {
   if (!dq || !dk || !dv) return ATTN_ERR_INVALID_ARG;
   if (((uintptr_t)dq & 3u) || ((uintptr_t)dk & 3u) || ((uintptr_t)dv & 3u)) return ATTN_ERR_UNSUPPORTED;
@@ -83,13 +102,29 @@ int validate_descales(const float* dq, const float* dk, const float* dv) {
 // XCD's 32 CUs, and head by head would leave the longest tiles of the last
 // heads to a few CUs at the end (1.5x the balanced time for B=4, H=16,
 // N=2048, in-order dispatch to 32 CUs).
+//
+// Fixed-length calls with that order and more items than the device has
+// compute units launch one work-group per compute unit instead, each
+// looping over its XCD's items (item_of, attn_kernels.hpp).  The hardware
+// starts a new work-group on a compute unit several microseconds after the
+// last one ends, and a causal call's items differ in length, so with one
+// work-group per item these gaps took 2-6% of each compute unit's time.
 int plan(attn::FwdParams& prm, int rows_per_block, int causal, int* grid_out) {
   const int64_t tiles = ((int64_t)prm.maxlen + rows_per_block - 1) / rows_per_block;
-  const int64_t grid = (int64_t)prm.B * prm.H * tiles;
+  int64_t grid = (int64_t)prm.B * prm.H * tiles;
   if (grid > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
   prm.n_qtiles = (int)tiles;
   prm.remap = (grid % 8 == 0) ? 1 : 0;
   if (prm.remap && causal && !prm.cu && tiles < 32 && ((int64_t)prm.B * prm.H) % 8 == 0) prm.remap = 2;
+  prm.items = (int)grid;
+  prm.persist = 0;
+  if (prm.remap && !prm.cu) {
+    const int cus = device_compute_units();
+    if (cus >= 8 && cus % 8 == 0 && grid > cus) {
+      prm.persist = 1;
+      grid = cus;
+    }
+  }
   *grid_out = (int)grid;
   return ATTN_OK;
 }

@@ -91,12 +91,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
+  // one work item (batch*head, query tile) per step; the loop runs once
+  // unless the launch is persistent.  The item's first loads go into LDS
+  // only after every wave has passed the previous item's last barrier.
+  for (int step = 0;; ++step) {
+  int L;
+  if (!item_of(p, step, L)) break;
   int bh, qt;
-  block_to_work(p, bh, qt);
+  block_to_work(p, L, bh, qt);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   SeqView sv;
-  if (!seq_view(p, D, b, h, qt * BR, sv)) return;   // whole work-group, before any barrier
+  if (!seq_view(p, D, b, h, qt * BR, sv)) continue;   // whole work-group, before any barrier
   const int N = sv.N;
   const long long tok = (long long)p.H * D;       // elements between tokens of Q and O
   const long long tkv = (long long)p.Hkv * D;     // elements between tokens of K and V
@@ -221,51 +227,47 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     constexpr bool QK = decltype(qk_tag)::value;
     constexpr bool PV = decltype(pv_tag)::value;
     // the matrix-core phase issues first on its SIMD; the partner wave's
-    // vector ALU work fills the remaining issue slots
+    // vector ALU work fills the remaining issue slots.  One stream of
+    // products, the S^T ones (ks-major) then the P.V ones, each operand read
+    // from LDS PF products ahead of its MFMA (a fence after every MFMA keeps
+    // that order whatever code surrounds the phase).
+    constexpr int PF = 6;
+    constexpr int NQ = QK ? NKS * NKB : 0;
+    constexpr int NP = NQ + (PV ? NKK * NDB : 0);
+    bf16x8 a[NP];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      if (i < NQ) {
+        const int ks = i / NKB, kb = i % NKB;
+        a[i] = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
+      } else {
+        const int kk = (i - NQ) / NDB, db = (i - NQ) % NDB;
+        const __bf16* vb = vt + kk * 16 * D + voff[db];
+        i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb));
+        i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb + 8 * D));
+        i32x4 w;
+        w[0] = (int)(unsigned short)lo[0] | ((int)(unsigned short)lo[1] << 16);
+        w[1] = (int)(unsigned short)lo[2] | ((int)(unsigned short)lo[3] << 16);
+        w[2] = (int)(unsigned short)hi[0] | ((int)(unsigned short)hi[1] << 16);
+        w[3] = (int)(unsigned short)hi[2] | ((int)(unsigned short)hi[3] << 16);
+        a[i] = __builtin_bit_cast(bf16x8, w);
+      }
+    };
     __builtin_amdgcn_s_setprio(3);
-    if constexpr (QK) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+    for (int i = 0; i < PF && i < NP; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          bf16x8 a = *(const bf16x8*)(kt + kb * 32 * D + koff[ks]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks == 0 ? f32x16{} : s[kb], 0,
-                                                         0, 0);
-        }
+    for (int i = 0; i < NP; ++i) {
+      if (i + PF < NP) rd(i + PF);
+      if (i < NQ) {
+        const int ks = i / NKB, kb = i % NKB;
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], qf[ks], ks == 0 ? f32x16{} : s[kb], 0,
+                                                       0, 0);
+      } else {
+        const int kk = (i - NQ) / NDB, db = (i - NQ) % NDB;
+        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], pf[kk], oacc[db], 0, 0, 0);
       }
-    }
-    if constexpr (PV) {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const __bf16* vb = vt + kk * 16 * D + voff[db];
-          i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb));
-          i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS i16x4*)(vb + 8 * D));
-          i32x4 w;
-          w[0] = (int)(unsigned short)lo[0] | ((int)(unsigned short)lo[1] << 16);
-          w[1] = (int)(unsigned short)lo[2] | ((int)(unsigned short)lo[3] << 16);
-          w[2] = (int)(unsigned short)hi[0] | ((int)(unsigned short)hi[1] << 16);
-          w[3] = (int)(unsigned short)hi[2] | ((int)(unsigned short)hi[3] << 16);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[kk],
-                                                            oacc[db], 0, 0, 0);
-        }
-      }
-    }
-    // keep several LDS fragments in flight ahead of the MFMAs that consume
-    // them (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA)
-    if constexpr (QK && PV) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-#pragma unroll
-      for (int i = 0; i < NKB * NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < NKK * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -505,6 +507,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       p.lse[sv.lse_base + myq] = (m_ref + fast_log2(l_tot)) * 0.69314718055994531f;
     }
   }
+  }   // work items
 }
 
 // ---------------------------------------------------------------------------

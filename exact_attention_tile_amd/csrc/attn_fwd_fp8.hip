@@ -98,12 +98,20 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   const int ln = lane & 31;
   const int lh = lane >> 5;
 
+  // one work item (batch*head, query tile) per step; the loop runs once
+  // unless the launch is persistent (never for the row-maximum pass, which
+  // is compiled without the loop).  The item's first loads go into LDS
+  // only after every wave has passed the previous item's last barrier.
+  constexpr int kMaxSteps = MODE == 1 ? 1 : 0x7fffffff;
+  for (int step = 0; step < kMaxSteps; ++step) {
+  int L;
+  if (!item_of(p, step, L)) break;
   int bh, qt;
-  block_to_work(p, bh, qt);
+  block_to_work(p, L, bh, qt);
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   SeqView sv;
-  if (!seq_view(p, D, b, h, qt * BR, sv)) return;   // whole work-group, before any barrier
+  if (!seq_view(p, D, b, h, qt * BR, sv)) continue;   // whole work-group, before any barrier
   const int N = sv.N;
   const long long tok = (long long)p.H * D;       // elements between tokens of Q and O
   const long long tkv = (long long)p.Hkv * D;     // elements between tokens of K and V
@@ -242,8 +250,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     constexpr bool PV = decltype(pv_tag)::value;
     // the matrix-core phase issues first on its SIMD; the partner wave's
     // vector ALU work fills the remaining issue slots
-    __builtin_amdgcn_s_setprio(3);
-    if constexpr (QK) {
+    if constexpr (!PV) {
+      // scores only (the first phase, and the row-maximum pass): left to the
+      // compiler's schedule
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
@@ -257,38 +267,53 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
                                                                  0, 0, 0, 0, 0, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
+      return;
     }
-    if constexpr (PV) {
+    // One stream of products, the S^T ones (ks-major, if QK) then the P.V
+    // ones, each operand read from LDS PF products ahead of its MFMA (a
+    // fence after every MFMA keeps that order whatever code surrounds the
+    // phase).
+    constexpr int PF = 2;
+    constexpr int NQ = QK ? NKS * NKB : 0;
+    constexpr int NP = NQ + NKK * NDB;
+    i32x8 a[NP];
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      i32x8 t;
+      if (i < NQ) {
+        const int ks = i / NKB, kb = i % NKB;
+        const u32x4 a0 = *(const u32x4*)(kt + kb * 32 * D + koff[ks][0]);
+        const u32x4 a1 = *(const u32x4*)(kt + kb * 32 * D + koff[ks][1]);
+        t[0] = a0[0]; t[1] = a0[1]; t[2] = a0[2]; t[3] = a0[3];
+        t[4] = a1[0]; t[5] = a1[1]; t[6] = a1[2]; t[7] = a1[3];
+      } else {
+        const int kk = (i - NQ) / NDB, db = (i - NQ) % NDB;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          i32x8 a;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (ATTN_LDS i32x2*)(vt + kk * 64 * D + voff[db] + 8 * u * D));
-            a[2 * u] = t[0];
-            a[2 * u + 1] = t[1];
-          }
-          oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pf[kk], oacc[db], 0, 0, 0, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+          const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              (ATTN_LDS i32x2*)(vt + kk * 64 * D + voff[db] + 8 * u * D));
+          t[2 * u] = r[0];
+          t[2 * u + 1] = r[1];
         }
       }
-    }
-    // keep LDS reads in flight ahead of the MFMAs that consume them
-    // (sched_group_barrier masks: 0x100 LDS read, 0x008 MFMA)
-    if constexpr (QK && PV) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+      a[i] = t;
+    };
+    __builtin_amdgcn_s_setprio(3);
 #pragma unroll
-      for (int i = 0; i < NKB * NKS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
+    for (int i = 0; i < PF && i < NP; ++i) rd(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NKK * NDB; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    for (int i = 0; i < NP; ++i) {
+      if (i + PF < NP) rd(i + PF);
+      if (i < NQ) {
+        const int ks = i / NKB, kb = i % NKB;
+        s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], qf[ks], ks == 0 ? f32x16{} : s[kb],
+                                                               0, 0, 0, 0, 0, 0);
+      } else {
+        const int kk = (i - NQ) / NDB, db = (i - NQ) % NDB;
+        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], pf[kk], oacc[db], 0, 0, 0, 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -479,7 +504,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
 
   if constexpr (MODE == 1) {
     if (myq < N && lh == 0) p.lse[sv.lse_base + myq] = m_ref;
-    return;
+    continue;
   }
   // ---- epilogue: O = acc dv / l -> bf16, lse = ln2 (m_ref - offset + log2 l)
   const float l_tot = pair_sum((l_part[0] + l_part[1]) + (l_part[2] + l_part[3]));
@@ -502,6 +527,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
           (m_ref - (MODE == 2 ? kPOffset2 : kPOffset) + fast_log2(l_tot)) * 0.69314718055994531f;
     }
   }
+  }   // work items
 }
 
 template <int D, int NW, int BC, bool CAUSAL>
@@ -509,8 +535,11 @@ static hipError_t launch_fp8_t(const FwdParams& prm, int grid, bool two_pass, hi
   if (!two_pass)
     return launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 0>, dim3(grid), dim3(NW * 64),
                          stream, prm);
-  const hipError_t e = launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 1>, dim3(grid),
-                                     dim3(NW * 64), stream, prm);
+  // the row-maximum pass: one work-group per item (its items are short)
+  FwdParams one = prm;
+  one.persist = 0;
+  const hipError_t e = launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 1>, dim3(prm.items),
+                                     dim3(NW * 64), stream, one);
   if (e != hipSuccess) return e;
   return launch_kernel(attn_fwd_fp8_kernel<D, NW, BC, CAUSAL, 2>, dim3(grid), dim3(NW * 64),
                        stream, prm);

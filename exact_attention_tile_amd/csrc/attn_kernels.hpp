@@ -38,7 +38,9 @@ struct FwdParams {
   int total;         // variable-length calls: tokens in the packed tensors
   int maxlen;        // longest sequence (N for fixed-length calls)
   int n_qtiles;      // ceil(maxlen / rows per workgroup)
-  int remap;         // XCD-aware block order (grid divisible by 8): 1 head-major, 2 tile-major
+  int remap;         // XCD-aware block order (items divisible by 8): 1 head-major, 2 tile-major
+  int items;         // work items: (batch*head, query tile) pairs of the block order
+  int persist;       // 1: gridDim.x work-groups (a multiple of 8) loop over the items
   float c;           // |scale| * log2(e): scores are kept in log2 units
   unsigned qsign;    // sign-flip mask applied to Q when scale < 0
 };
@@ -122,9 +124,8 @@ __device__ __forceinline__ int seq_by_rank(const int* cu, int B, int r) {
   return 0;   // unreachable: the ranks are a permutation of 0 .. B-1
 }
 
-__device__ __forceinline__ void block_to_work(const FwdParams& p, int& bh, int& qt) {
-  int total = gridDim.x;
-  int L = blockIdx.x;
+__device__ __forceinline__ void block_to_work(const FwdParams& p, int L, int& bh, int& qt) {
+  const int total = p.items;
   if (p.cu) {
     const int BH = p.B * p.H;
     if ((p.H & 7) == 0 && p.B <= 128) {
@@ -164,6 +165,28 @@ __device__ __forceinline__ void block_to_work(const FwdParams& p, int& bh, int& 
   }
   bh = L / p.n_qtiles;
   qt = p.n_qtiles - 1 - (L - bh * p.n_qtiles);
+}
+
+// Work item L of this work-group's step s.  One work-group per item
+// (persist 0): the work-group's own index, step 0 only.  Persistent launch
+// (gridDim.x work-groups, a multiple of 8, one per compute unit): item L
+// belongs to XCD L % 8 in the block order, and work-group g runs on XCD
+// g % 8, so each XCD's W = gridDim.x / 8 work-groups take that XCD's items
+// (local index k = L / 8, longest first) in rounds of W.  The order within
+// a round is serpentine: work-group j takes the j-th item in even rounds
+// and the (W-1-j)-th in odd ones, which pairs long causal tiles with short
+// ones.  Returns false once the XCD's items are used up.
+__device__ __forceinline__ bool item_of(const FwdParams& p, int s, int& L) {
+  if (!p.persist) {
+    L = blockIdx.x;
+    return s == 0;
+  }
+  const int g = blockIdx.x;
+  const int j = g >> 3, W = gridDim.x >> 3;
+  const int k = s * W + ((s & 1) ? W - 1 - j : j);
+  if (k >= (p.items >> 3)) return false;
+  L = (g & 7) + 8 * k;
+  return true;
 }
 
 // The two lane halves of a wave hold the same query column; these combine

@@ -1,8 +1,9 @@
 """Work order and mask segments of the attention kernels, as a Python model.
 
 These tests check a Python restatement of the device and host logic, not the
-compiled code: plan_remap / block_order below re-implement plan()
-(attn_api.cpp) and block_to_work (attn_kernels.hpp), and the segment bounds
+compiled code: plan_remap / plan_persist / block_to_work / item_of below
+re-implement plan() (attn_api.cpp), block_to_work and item_of
+(attn_kernels.hpp), and the segment bounds
 re-implement the kernels' loop limits.  They pin the design -- that the
 chosen orders are bijections and that the segment bounds agree with the
 per-tile mask definition -- so a change to the model that breaks it fails
@@ -11,9 +12,11 @@ every parity test covers each query tile's rows (sampled or whole) and the
 guard bands around O and LSE, so a launch index mapped twice or never shows
 there as a wrong or missing row.
 
-Block order: the fixed-length forward kernels must map every launch index to
+Block order: the fixed-length forward kernels must map every item index to
 a distinct (batch*head, query tile) pair, so that each query tile is
-computed exactly once.
+computed exactly once; in a persistent launch every item must be taken by
+exactly one work-group, on its own XCD, and a causal call's work must
+spread evenly over the work-groups.
 
 Mask segments: the forward, dQ and dK/dV tile loops run the tiles that need
 no mask through a body without it; the segment bounds must agree with the
@@ -56,6 +59,62 @@ def test_block_order_is_a_bijection(causal):
         seen = {block_to_work(L, grid, B, H, tiles, remap) for L in range(grid)}
         assert len(seen) == grid, (B, H, N, causal)
         assert all(0 <= bh < B * H and 0 <= qt < tiles for bh, qt in seen)
+
+
+def plan_persist(grid, remap, cus):
+    """plan(): one work-group per compute unit when the block order is
+    XCD-aware (fixed-length calls) and there are more items than units."""
+    return remap != 0 and cus >= 8 and cus % 8 == 0 and grid > cus
+
+
+def item_of(g, s, G, items):
+    """item_of (attn_kernels.hpp): item of persistent work-group g at step s,
+    or None past its XCD's last item."""
+    j, W = g >> 3, G >> 3
+    k = s * W + (W - 1 - j if s & 1 else j)
+    if k >= items >> 3:
+        return None
+    return (g & 7) + 8 * k
+
+
+def persistent_schedule(grid, cus):
+    """Items of each work-group, in its order."""
+    out = []
+    for g in range(cus):
+        mine, s = [], 0
+        while True:
+            L = item_of(g, s, cus, grid)
+            if L is None:
+                break
+            mine.append(L)
+            s += 1
+        out.append(mine)
+    return out
+
+
+@pytest.mark.parametrize("cus", (256, 64, 8))
+def test_persistent_order_covers_every_item_once(cus):
+    for B, H, N in SHAPES:
+        for causal in (False, True):
+            tiles, grid, remap = plan_remap(B, H, N, causal)
+            if not plan_persist(grid, remap, cus):
+                continue
+            sched = persistent_schedule(grid, cus)
+            flat = [L for mine in sched for L in mine]
+            assert sorted(flat) == list(range(grid)), (B, H, N, causal, cus)
+            # a work-group stays on its XCD's items
+            assert all(L % 8 == g % 8 for g, mine in enumerate(sched) for L in mine)
+
+
+@pytest.mark.parametrize("B,H,N", [(2, 16, 8192), (1, 32, 32768), (4, 16, 2048), (2, 32, 8192)])
+def test_persistent_order_balances_causal_work(B, H, N):
+    # work of an item: the 64-key tiles its 256 query rows see (causal)
+    tiles, grid, remap = plan_remap(B, H, N, True)
+    assert plan_persist(grid, remap, 256)
+    sched = persistent_schedule(grid, 256)
+    work = [sum((block_to_work(L, grid, B, H, tiles, remap)[1] + 1) * 4 for L in mine)
+            for mine in sched]
+    assert max(work) <= 1.03 * (sum(work) / len(work)), (B, H, N, max(work), min(work))
 
 
 def test_tile_major_order_for_short_causal_calls():
