@@ -26,7 +26,7 @@ hipError_t launch_fp8(const FwdParams& prm, int d, int causal, int grid, bool tw
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* delta, int B, int H, int N, int d, int causal, float scale,
-                           hipStream_t stream);
+                           int cus, hipStream_t stream);
 hipError_t launch_quant(const void* x, void* codes, float* descale, const unsigned* signs, int B,
                         int N, int H, int d, hipStream_t stream);
 }  // namespace attn
@@ -291,7 +291,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   const int64_t grid = (int64_t)B * H * ((N + 127) / 128);   // the larger of the kernels' grids
   if (grid > INT32_MAX || (tokens * H + 15) / 16 > INT32_MAX) return ATTN_ERR_UNSUPPORTED;
   const hipError_t e = attn::launch_bwd_bf16(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N,
-                                             d, causal, scale, stream);
+                                             d, causal, scale, device_compute_units(), stream);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

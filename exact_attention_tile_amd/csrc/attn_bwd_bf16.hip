@@ -56,6 +56,8 @@ struct BwdParams {
   int n_tiles;       // ceil(N / 256): query tiles per head (dQ)
   int n_ktiles;      // ceil(N / 256): key tiles per head (dK/dV)
   int tile_major;    // 1: tile-major block order (see bwd_work)
+  int items;         // work items of the kernel launched: (batch*head, tile) pairs
+  int persist;       // 1: gridDim.x work-groups (a multiple of 8) loop over the items
   float c;           // scale * log2(e)
   float scale;
 };
@@ -174,8 +176,7 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // contiguous logical range [x G/8, (x+1) G/8) puts all tiles of a head on
 // one L2, which then serves the K/V (or Q/dO) tiles every work-group of
 // that head streams.
-__device__ __forceinline__ int xcd_order(int L) {
-  const int total = gridDim.x;
+__device__ __forceinline__ int xcd_order(int L, int total) {
   if ((total & 7) != 0) return L;
   return (L & 7) * (total >> 3) + (L >> 3);
 }
@@ -186,8 +187,7 @@ __device__ __forceinline__ int xcd_order(int L) {
 // their causal tile lengths do not pair up over an XCD's 32 CUs, so each XCD
 // keeps its share of the heads but runs the longest tile of every head
 // first, then the next longest.
-__device__ __forceinline__ void bwd_work(const BwdParams& p, int n, int& bh, int& rank) {
-  const int L = blockIdx.x;
+__device__ __forceinline__ void bwd_work(const BwdParams& p, int n, int L, int& bh, int& rank) {
   if (p.tile_major) {
     const int hx = (p.B * p.H) >> 3;
     const int k = L >> 3;
@@ -195,7 +195,7 @@ __device__ __forceinline__ void bwd_work(const BwdParams& p, int n, int& bh, int
     bh = (L & 7) * hx + (k - rank * hx);
     return;
   }
-  const int Lx = xcd_order(L);
+  const int Lx = xcd_order(L, p.items);
   bh = Lx / n;
   rank = Lx - bh * n;
 }
@@ -265,7 +265,7 @@ __device__ __forceinline__ void store_rows(__bf16* dst, const f32x16 (&acc)[NDB]
 // ---------------------------------------------------------------------------
 // dQ: per (batch, head, 256 query rows); 64-key K/V tiles
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOOP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int BR = 256, BC = 64;
@@ -275,14 +275,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   __bf16* ks_base = smem;
   __bf16* vs_base = smem + 2 * TILE;
 
-  const int tid = threadIdx.x;
+  // one work item per step.  LOOP (persistent launches, item_of_n): an
+  // item's first loads go into LDS only after every wave has passed the
+  // previous item's last barrier, and the lane's values are derived anew in
+  // every item (taken out of the loop they would stay live through it and
+  // cost registers).  Without LOOP the body is compiled straight, once.
+  constexpr int kMaxSteps = LOOP ? 0x7fffffff : 1;
+  for (int step = 0; step < kMaxSteps; ++step) {
+  int L;
+  if (!item_of_n(p.items, p.persist, step, L)) break;
+  int tid = threadIdx.x;
+  if constexpr (LOOP) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int ln = lane & 31;
   const int lh = lane >> 5;
-
   int bh, rank;
-  bwd_work(p, p.n_tiles, bh, rank);
+  bwd_work(p, p.n_tiles, L, bh, rank);
   const int qt = p.n_tiles - 1 - rank;   // longest first
   const int b = bh / p.H;
   const int h = bh - b * p.H;
@@ -458,6 +467,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
   }
 
   if (myq < N) store_rows<NDB>((__bf16*)p.dq + head_base + (long long)myq * tok, acc, p.scale, lh);
+  }   // work items
 }
 
 // ---------------------------------------------------------------------------
@@ -467,7 +477,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dq_kernel(BwdParams p) {
 // these do not fit the 256 registers of a wave that shares its SIMD:
 // attn_bwd_dkdv_pair_kernel below splits the work between two waves).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOOP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   static_assert(D == 64, "head dim 64 (128: attn_bwd_dkdv_pair_kernel)");
   constexpr bool DV = true;
@@ -481,14 +491,23 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   __bf16* qs_base = smem;
   __bf16* gs_base = smem + 2 * TILE;
 
-  const int tid = threadIdx.x;
+  // one work item per step.  LOOP (persistent launches, item_of_n): an
+  // item's first loads go into LDS only after every wave has passed the
+  // previous item's last barrier, and the lane's values are derived anew in
+  // every item (taken out of the loop they would stay live through it and
+  // cost registers).  Without LOOP the body is compiled straight, once.
+  constexpr int kMaxSteps = LOOP ? 0x7fffffff : 1;
+  for (int step = 0; step < kMaxSteps; ++step) {
+  int L;
+  if (!item_of_n(p.items, p.persist, step, L)) break;
+  int tid = threadIdx.x;
+  if constexpr (LOOP) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int ln = lane & 31;
   const int lh = lane >> 5;
-
   int bh, kt;
-  bwd_work(p, p.n_ktiles, bh, kt);      // causal: low key tiles see the most queries
+  bwd_work(p, p.n_ktiles, L, bh, kt);   // causal: low key tiles see the most queries
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -712,6 +731,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
     if constexpr (DK) store_rows<NDB>((__bf16*)p.dk + head_base + (long long)mykey * tok, dk, p.scale, lh);
     if constexpr (DV) store_rows<NDB>((__bf16*)p.dv + head_base + (long long)mykey * tok, dv, 1.f, lh);
   }
+  }   // work items
 }
 
 // ---------------------------------------------------------------------------
@@ -741,7 +761,7 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
 // phase before it; the swizzled offsets of k-step ks and column block db are
 // the first ones XOR 16 ks and XOR 32 db (elements).
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool LOOP>
 __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int KW = 4;                   // key groups of 32 (one per SIMD)
@@ -755,16 +775,25 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
   __shared__ __attribute__((aligned(16))) f32x4 pbuf[KW][8][64];   // [key group][(qb, quarter)][lane]
   __shared__ __attribute__((aligned(16))) float rowv[NB][2][BQ];   // [buffer][lse2, D][query]
 
-  const int tid = threadIdx.x;
+  // one work item per step.  LOOP (persistent launches, item_of_n): an
+  // item's first loads go into LDS only after every wave has passed the
+  // previous item's last barrier, and the lane's values are derived anew in
+  // every item (taken out of the loop they would stay live through it and
+  // cost registers).  Without LOOP the body is compiled straight, once.
+  constexpr int kMaxSteps = LOOP ? 0x7fffffff : 1;
+  for (int step = 0; step < kMaxSteps; ++step) {
+  int L;
+  if (!item_of_n(p.items, p.persist, step, L)) break;
+  int tid = threadIdx.x;
+  if constexpr (LOOP) asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches
   const int role = wave >> 2;                                  // 0: P wave, 1: dS wave
   const int kgrp = wave & 3;
   const int ln = lane & 31;
   const int lh = lane >> 5;
-
   int bh, kt;
-  bwd_work(p, p.n_ktiles, bh, kt);      // causal: low key tiles see the most queries
+  bwd_work(p, p.n_ktiles, L, bh, kt);   // causal: low key tiles see the most queries
   const int b = bh / p.H;
   const int h = bh - b * p.H;
   const int N = p.N;
@@ -1111,34 +1140,58 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
     __bf16* dst = (__bf16*)(role ? p.dk : p.dv) + head_base + (long long)mykey * tok;
     store_rows<NDB>(dst, acc, role ? p.scale : 1.f, lh);
   }
+  }   // work items
 }
 
 // ---------------------------------------------------------------------------
 // host-side launch (called by the C ABI in attn_api.cpp)
 // ---------------------------------------------------------------------------
+// The grid of a kernel with `items` work items: one work-group per item,
+// or, for causal calls with more items than the device's `cus` compute
+// units (a multiple of 8) and an XCD-aware order, one work-group per
+// compute unit looping over the items (item_of_n).  Causal items differ in
+// length, and a new work-group starts on a compute unit several
+// microseconds after the last one ends; non-causal items are all alike and
+// measured slightly faster one work-group per item.
+// (Only causal launches loop, so the looping kernels are instantiated with
+// LOOP = CAUSAL.)
+static int bwd_grid(BwdParams& prm, int items, int cus, bool causal) {
+  prm.items = items;
+  prm.persist = (causal && cus >= 8 && cus % 8 == 0 && items % 8 == 0 && items > cus) ? 1 : 0;
+  return prm.persist ? cus : items;
+}
+
 template <int D, bool CAUSAL>
-static hipError_t launch_bwd_t(BwdParams prm, hipStream_t stream) {
+static hipError_t launch_bwd_t(BwdParams prm, int cus, hipStream_t stream) {
   const long long rows = (long long)prm.B * prm.N * prm.H;
   const int grid_delta = (int)((rows + 15) / 16);
   hipError_t e = launch_kernel(attn_bwd_delta_kernel<D>, dim3(grid_delta), dim3(256), stream, prm);
   if (e != hipSuccess) return e;
-  const int grid = prm.B * prm.H * prm.n_tiles;
-  e = launch_kernel(attn_bwd_dq_kernel<D, CAUSAL>, dim3(grid), dim3(512), stream, prm);
+  int grid = bwd_grid(prm, prm.B * prm.H * prm.n_tiles, cus, CAUSAL);
+  e = prm.persist
+          ? launch_kernel(attn_bwd_dq_kernel<D, CAUSAL, CAUSAL>, dim3(grid), dim3(512), stream, prm)
+          : launch_kernel(attn_bwd_dq_kernel<D, CAUSAL, false>, dim3(grid), dim3(512), stream, prm);
   if (e != hipSuccess) return e;
   if constexpr (D == 128) {
     prm.n_ktiles = (prm.N + 127) / 128;
-    return launch_kernel(attn_bwd_dkdv_pair_kernel<D, CAUSAL>, dim3(prm.B * prm.H * prm.n_ktiles),
-                         dim3(512), stream, prm);
+    grid = bwd_grid(prm, prm.B * prm.H * prm.n_ktiles, cus, CAUSAL);
+    return prm.persist ? launch_kernel(attn_bwd_dkdv_pair_kernel<D, CAUSAL, CAUSAL>, dim3(grid),
+                                       dim3(512), stream, prm)
+                       : launch_kernel(attn_bwd_dkdv_pair_kernel<D, CAUSAL, false>, dim3(grid),
+                                       dim3(512), stream, prm);
   } else {
     prm.n_ktiles = prm.n_tiles;
-    return launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL>, dim3(grid), dim3(512), stream, prm);
+    grid = bwd_grid(prm, prm.B * prm.H * prm.n_ktiles, cus, CAUSAL);
+    return prm.persist
+               ? launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, CAUSAL>, dim3(grid), dim3(512), stream, prm)
+               : launch_kernel(attn_bwd_dkdv_kernel<D, CAUSAL, false>, dim3(grid), dim3(512), stream, prm);
   }
 }
 
 hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            float* delta, int B, int H, int N, int d, int causal, float scale,
-                           hipStream_t stream) {
+                           int cus, hipStream_t stream) {
   BwdParams prm = {};
   prm.q = q;
   prm.k = k;
@@ -1157,8 +1210,9 @@ hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const vo
   prm.tile_major = causal && prm.n_tiles < 32 && (B * H) % 8 == 0;
   prm.scale = scale;
   prm.c = scale * kLog2e;
-  if (d == 128) return causal ? launch_bwd_t<128, true>(prm, stream) : launch_bwd_t<128, false>(prm, stream);
-  return causal ? launch_bwd_t<64, true>(prm, stream) : launch_bwd_t<64, false>(prm, stream);
+  if (d == 128)
+    return causal ? launch_bwd_t<128, true>(prm, cus, stream) : launch_bwd_t<128, false>(prm, cus, stream);
+  return causal ? launch_bwd_t<64, true>(prm, cus, stream) : launch_bwd_t<64, false>(prm, cus, stream);
 }
 
 }  // namespace attn

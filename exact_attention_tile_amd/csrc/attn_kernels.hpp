@@ -176,17 +176,20 @@ __device__ __forceinline__ void block_to_work(const FwdParams& p, int L, int& bh
 // a round is serpentine: work-group j takes the j-th item in even rounds
 // and the (W-1-j)-th in odd ones, which pairs long causal tiles with short
 // ones.  Returns false once the XCD's items are used up.
-__device__ __forceinline__ bool item_of(const FwdParams& p, int s, int& L) {
-  if (!p.persist) {
+__device__ __forceinline__ bool item_of_n(int items, int persist, int s, int& L) {
+  if (!persist) {
     L = blockIdx.x;
     return s == 0;
   }
   const int g = blockIdx.x;
   const int j = g >> 3, W = gridDim.x >> 3;
   const int k = s * W + ((s & 1) ? W - 1 - j : j);
-  if (k >= (p.items >> 3)) return false;
+  if (k >= (items >> 3)) return false;
   L = (g & 7) + 8 * k;
   return true;
+}
+__device__ __forceinline__ bool item_of(const FwdParams& p, int s, int& L) {
+  return item_of_n(p.items, p.persist, s, L);
 }
 
 // The two lane halves of a wave hold the same query column; these combine

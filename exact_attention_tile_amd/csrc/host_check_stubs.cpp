@@ -16,7 +16,7 @@ hipError_t launch_fp8(const FwdParams&, int, int, int, bool, hipStream_t) {
 }
 hipError_t launch_bwd_bf16(const void*, const void*, const void*, const void*, const float*,
                            const void*, void*, void*, void*, float*, int, int, int, int, int, float,
-                           hipStream_t) {
+                           int, hipStream_t) {
   return hipErrorNotSupported;
 }
 hipError_t launch_quant(const void*, void*, float*, const unsigned*, int, int, int, int,
