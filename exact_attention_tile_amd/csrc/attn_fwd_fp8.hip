@@ -135,6 +135,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     qsign ^= 0x80808080u;
   }
   c = fmaxf(c, 1e-30f);
+  // c is uniform over the work-group: in a scalar register, the softmax's
+  // FMAs read two vector operands instead of three
+  c = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
 
   // ---- Q^T fragments: lane (n=ln, h=lh) holds Q[myq][64ks + 32lh .. +31]
   i32x8 qf[NKS];
