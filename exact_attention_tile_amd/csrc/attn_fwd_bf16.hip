@@ -163,11 +163,19 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS __bf16*)ks_base);
   const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS __bf16*)vs_base);
   const unsigned lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wb * LPW * 1024));
+  // The loads' addresses are scalar work of the loading wave's vector phase,
+  // where a lone wave issues every instruction slowly: a tile's byte offset
+  // is one 32x32 -> 64-bit product of the tile index and the tile's bytes
+  // (BC tokens of K or V), and a full tile is one compare against the
+  // count of full tiles.
+  const unsigned tile_bytes = (unsigned)(BC * 2) * (unsigned)tkv;
+  const int n_full = N / BC;
   auto load_tile = [&](const unsigned* go, const __bf16* src, unsigned lds_buf, int j) {
     const int kv0 = j * BC;
     const unsigned la0 = lds_buf + lds_wave;
-    if (kv0 + BC <= N) {
-      const __bf16* base = src + (long long)kv0 * tkv;
+    if (__builtin_expect(j < n_full, 1)) {
+      const __bf16* base =
+          (const __bf16*)((const char*)src + (unsigned long long)(unsigned)j * tile_bytes);
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
@@ -357,7 +365,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       exponentials(t);
     } else {
       exponentials(t);
-      if (__builtin_amdgcn_ballot_w64(!(t[0] + t[1] <= kPMaxBf16))) {
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(t[0] + t[1] <= kPMaxBf16)) != 0, 0)) {
         rescale();
         exponentials(t);
       }
@@ -386,8 +394,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   const int n_phases = 2 * wg_tiles + 2;
   auto loads_for = [&](int u) {
     u = __builtin_amdgcn_readfirstlane(u);    // an SGPR for the loads' addresses
-    if (u + 1 < wg_tiles) load_k(u + 1);
-    if (u < wg_tiles) load_v(u);
+    if (__builtin_expect(u + 1 < wg_tiles, 1)) load_k(u + 1);
+    if (__builtin_expect(u < wg_tiles, 1)) load_v(u);
   };
   auto kt_of = [&](int j) { return ks_base + ((j + 1) & 1) * TILE; };   // K tile of X_j
   auto vt_of = [&](int j) { return vs_base + (j & 1) * TILE; };         // V tile of X_j

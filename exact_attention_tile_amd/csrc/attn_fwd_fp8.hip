@@ -190,11 +190,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
   const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS unsigned char*)ks_base);
   const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS unsigned char*)vs_base);
   const unsigned lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wb * LPW * 1024));
+  // a tile's byte offset: one 32x32 -> 64-bit product of the tile index and
+  // the tile's bytes (few scalar instructions in the loading phase); a full
+  // tile: one compare against the count of full tiles
+  const unsigned tile_bytes = (unsigned)BC * (unsigned)tkv;
+  const int n_full = N / BC;
   auto load_tile = [&](const unsigned* go, const int* key, const unsigned char* src, unsigned lds_buf, int j) {
     const int kv0 = j * BC;
     const unsigned la0 = lds_buf + lds_wave;
-    const unsigned char* base = src + (long long)kv0 * tkv;
-    if (kv0 + BC <= N) {
+    const unsigned char* base = src + (unsigned long long)(unsigned)j * tile_bytes;
+    if (__builtin_expect(j < n_full, 1)) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
