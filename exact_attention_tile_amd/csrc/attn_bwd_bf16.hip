@@ -146,10 +146,14 @@ struct TileLoader {
     lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wave * LPW * 1024));
   }
   // rows row0 .. row0+ROWS-1 of the tensor at src (element (row, 0) = src + row*tok)
+  // The byte offset of row0 is one 32x32 -> 64-bit product: the loads are
+  // issued in vector phases, where a lone wave issues every instruction
+  // slowly, scalar ones included.
   __device__ void load(const __bf16* src, long long tok, unsigned lds_buf, int row0, int N) const {
     const unsigned la0 = lds_buf + lds_wave;
-    const __bf16* base = src + (long long)row0 * tok;
-    if (row0 + ROWS <= N) {
+    const __bf16* base =
+        (const __bf16*)((const char*)src + (unsigned long long)(unsigned)row0 * (unsigned)(tok * 2));
+    if (__builtin_expect(row0 + ROWS <= N, 1)) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i)
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
