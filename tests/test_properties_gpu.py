@@ -11,7 +11,10 @@ the full size of the benchmark workloads and in their launch configuration
   D_i over queries i >= j, all of which depend on K_j and V_j and on the
   fixed inputs only);
 * independence of the (batch, head) problems: replacing one problem's K
-  and V leaves every other problem's O and LSE unchanged.
+  and V leaves every other problem's O and LSE unchanged; with grouped
+  K/V heads, replacing K/V head g changes exactly the query heads that
+  read it; with packed sequences, replacing one sequence's K and V changes
+  that sequence's rows only.
 
 Each follows from the definition of causal attention (a query attends to
 the keys at or before it, and each (batch, head) is its own problem), so
@@ -25,7 +28,7 @@ import pytest
 import torch
 
 import exact_attention_tile_amd as eat
-from parity_common import dev_u16, dev_u8, require_gpu, run_bf16, run_fp8
+from parity_common import Guarded, dev_u16, dev_u8, require_gpu, run_bf16, run_fp8
 from workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -124,3 +127,62 @@ def test_backward_causal_prefix(name):
     for name_g, a, b in zip(("dQ", "dK", "dV"), g0, g1):
         assert torch.equal(a[:, :p], b[:, :p]), "%s of a token before p changed" % name_g
     assert not torch.equal(g0[0][:, p:], g1[0][:, p:]), "dQ from p on did not see the new keys"
+
+
+def _run_grouped(w, inp, causal):
+    """gqa8k / varlen (bf16) through attn_fwd_gqa / attn_fwd_varlen; O and
+    LSE as integer views, O as [B or 1][tokens][H][d]."""
+    q, k, v = dev_u16(inp["q"]), dev_u16(inp["k"]), dev_u16(inp["v"])
+    s = torch.cuda.current_stream()
+    if w.varlen:
+        cu = torch.from_numpy(np.asarray(inp["cu"], dtype=np.int32)).cuda()
+        nseq = len(inp["cu"]) - 1
+        print("case %s sequences=%d total=%d H=%d Hkv=%d d=%d causal=%d" %
+              (w.name, nseq, w.total, w.H, w.kv_heads, w.d, causal), flush=True)
+        out = Guarded(1, w.total, w.H, w.d)
+        eat.attn_fwd_varlen(q, k, v, out.o_ptr, out.l_ptr, cu, nseq, w.total, w.N, w.H,
+                            w.kv_heads, w.d, int(causal), w.scale, s)
+    else:
+        print("case %s B=%d H=%d Hkv=%d N=%d d=%d causal=%d" %
+              (w.name, w.B, w.H, w.kv_heads, w.N, w.d, causal), flush=True)
+        out = Guarded(w.B, w.N, w.H, w.d)
+        eat.attn_fwd_gqa(q, k, v, out.o_ptr, out.l_ptr, w.B, w.H, w.kv_heads, w.N, w.d,
+                         int(causal), w.scale, s)
+    torch.cuda.synchronize()
+    assert out.guards_intact()
+    return out.o().view(torch.int16), out.lse().view(torch.int32)
+
+
+def test_grouped_kv_head_independence():
+    w = WORKLOADS["gqa8k"]
+    inp = make_inputs(w)
+    g = 5
+    o0, l0 = _run_grouped(w, inp, True)
+    o1, l1 = _run_grouped(w, _replacement(inp, "bf16", np.s_[:, :, g], 905), True)
+    group = w.H // w.kv_heads
+    for h in range(w.H):
+        same_o = torch.equal(o0[:, :, h], o1[:, :, h])
+        same_l = torch.equal(l0[:, h], l1[:, h])
+        if h // group == g:
+            assert not same_o, "query head %d did not see its new K/V head" % h
+        else:
+            assert same_o and same_l, "query head %d changed with K/V head %d" % (h, g)
+
+
+def test_varlen_sequence_independence():
+    w = WORKLOADS["varlen"]
+    inp = make_inputs(w)
+    cu = [int(x) for x in inp["cu"]]
+    lens = [cu[i + 1] - cu[i] for i in range(len(cu) - 1)]
+    s_rep = int(np.argsort(lens)[len(lens) // 2])       # a sequence of middling length
+    o0, l0 = _run_grouped(w, inp, True)
+    o1, l1 = _run_grouped(w, _replacement(inp, "bf16", np.s_[:, cu[s_rep]:cu[s_rep + 1]], 906),
+                          True)
+    for sq in range(len(lens)):
+        a, b = cu[sq], cu[sq + 1]
+        same = torch.equal(o0[:, a:b], o1[:, a:b]) and torch.equal(l0[:, :, a:b], l1[:, :, a:b])
+        if sq == s_rep:
+            assert lens[sq] == 0 or not torch.equal(o0[:, a:b], o1[:, a:b]), \
+                "the replaced sequence did not change"
+        else:
+            assert same, "sequence %d changed with sequence %d" % (sq, s_rep)
