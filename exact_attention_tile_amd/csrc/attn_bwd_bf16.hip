@@ -122,10 +122,12 @@ __global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdParams p) {
 }
 
 // Tile loader shared by the dQ and dK/dV kernels: NW waves each fill LPW
-// 1 KiB pieces of a [ROWS][D] bf16 tile with
-// global_load_lds_dwordx4 (lane l fills bytes [16 l, 16 l + 16) after the
-// wave-uniform base in M0), choosing each lane's source chunk so that the
-// tile lands swizzled; rows past N are clamped to row N-1.
+// 1 KiB pieces of a [ROWS][D] bf16 tile with global_load_lds_dwordx4
+// (lds_dma_*: lane l fills bytes [16 l, 16 l + 16) of a piece), choosing
+// each lane's source chunk so that the tile lands swizzled; rows past N are
+// clamped to row N-1.  The loads share M0 in groups of four, so the offset
+// of piece i is stored less 1024 (i % 4) (still >= 0: piece i starts at
+// least that many bytes into the tile).
 template <int D, int NW, int ROWS = 64>
 struct TileLoader {
   static constexpr int TILE = ROWS * D;
@@ -141,7 +143,7 @@ struct TileLoader {
       const int r = off / D;
       const int pc = (off - r * D) / 8;
       row[i] = r;
-      go[i] = (unsigned)(((long long)r * tok + (pc ^ swz_b<D>(r)) * 8) * 2);
+      go[i] = (unsigned)(((long long)r * tok + (pc ^ swz_b<D>(r)) * 8) * 2) - (unsigned)((i & 3) * 1024);
     }
     lds_wave = __builtin_amdgcn_readfirstlane((unsigned)(wave * LPW * 1024));
   }
@@ -154,20 +156,15 @@ struct TileLoader {
     const __bf16* base =
         (const __bf16*)((const char*)src + (unsigned long long)(unsigned)row0 * (unsigned)(tok * 2));
     if (__builtin_expect(row0 + ROWS <= N, 1)) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
-                     "v"(go[i]), "s"(base)
-                     : "memory");
+      lds_dma_tile_s<LPW>(la0, go, base);
     } else {
+      const void* g[LPW];
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const long long back = (long long)(row0 + row[i] < N ? 0 : row0 + row[i] - (N - 1)) * tok;
-        const __bf16* g = base + (long long)(go[i] / 2) - back;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
-                     "v"(g)
-                     : "memory");
+        g[i] = base + (long long)(go[i] / 2) - back;
       }
+      lds_dma_tile_v<LPW>(la0, g);
     }
   }
 };

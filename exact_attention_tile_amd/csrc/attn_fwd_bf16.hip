@@ -139,15 +139,17 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   }
 
   // ---- tile loader (group B only): global_load_lds_dwordx4 straight into
-  // the swizzled LDS tile.  One instruction fills 1 KiB of LDS, lane l
-  // writing bytes [16 l, 16 l + 16) after the wave-uniform base (M0), so the
-  // swizzle is applied by choosing each lane's source chunk.  Rows past N are
-  // clamped to row N-1: their keys are masked, so they contribute p = 0
-  // against finite V.  The loads are issued with inline asm so that the
-  // compiler does not serialise them against LDS reads of the other buffer;
-  // their completion is awaited explicitly (vmcnt) before a barrier.
+  // the swizzled LDS tile (lds_dma_*).  One instruction fills 1 KiB of LDS,
+  // lane l writing bytes [16 l, 16 l + 16) after the wave-uniform base, so
+  // the swizzle is applied by choosing each lane's source chunk.  Rows past
+  // N are clamped to row N-1: their keys are masked, so they contribute
+  // p = 0 against finite V.  Completion is awaited explicitly (vmcnt) before
+  // a barrier.  A wave's four loads of a tile share one M0 value, so each
+  // lane's offset for load i is stored less 1024 i (still >= 0: load i
+  // starts 1024 i bytes into the LDS tile, and at least that many bytes of
+  // global rows into the tile).
   constexpr int LPW = TILE * 2 / 1024 / 4;              // loads per B wave per tensor per tile
-  static_assert(LPW * 1024 * 4 == TILE * 2, "tile must split into 1 KiB per load");
+  static_assert(LPW == 4 && LPW * 1024 * 4 == TILE * 2, "tile must split into four 1 KiB loads per wave");
   const int wb = wave & 3;                               // index within the group
   int ld_row[LPW];
   unsigned kgo[LPW], vgo[LPW];
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
     const int row = off / D;
     const int pc = (off - row * D) / 8;                   // physical 16-byte chunk
     ld_row[i] = row;
-    kgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_k<D>(row)) * 8) * 2);
-    vgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_v<D>(row)) * 8) * 2);
+    kgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_k<D>(row)) * 8) * 2) - (unsigned)(i * 1024);
+    vgo[i] = (unsigned)(((long long)row * tkv + (pc ^ swz_v<D>(row)) * 8) * 2) - (unsigned)(i * 1024);
   }
   const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS __bf16*)ks_base);
   const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS __bf16*)vs_base);
@@ -170,28 +172,25 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   // count of full tiles.
   const unsigned tile_bytes = (unsigned)(BC * 2) * (unsigned)tkv;
   const int n_full = N / BC;
+  // a full tile: the wave's four loads from the tile at global address base
+  auto load_full = [&](const unsigned* go, const void* base, unsigned la0) {
+    lds_dma_s<LPW>(la0, go, base);
+  };
   auto load_tile = [&](const unsigned* go, const __bf16* src, unsigned lds_buf, int j) {
     const int kv0 = j * BC;
     const unsigned la0 = lds_buf + lds_wave;
     if (__builtin_expect(j < n_full, 1)) {
-      const __bf16* base =
-          (const __bf16*)((const char*)src + (unsigned long long)(unsigned)j * tile_bytes);
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
-                     "v"(go[i]), "s"(base)
-                     : "memory");
+      load_full(go, (const char*)src + (unsigned long long)(unsigned)j * tile_bytes, la0);
     } else {
       // ragged last tile: clamp the rows (64-bit addresses)
       const __bf16* base = src + (long long)kv0 * tkv;
+      const void* g[LPW];
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const long long back = (long long)(kv0 + ld_row[i] < N ? 0 : kv0 + ld_row[i] - (N - 1)) * tkv;
-        const __bf16* g = base + (long long)(go[i] / 2) - back;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
-                     "v"(g)
-                     : "memory");
+        g[i] = base + (long long)(go[i] / 2) - back;
       }
+      lds_dma_v<LPW>(la0, g);
     }
   };
   auto load_k = [&](int j) { load_tile(kgo, kg, lds_k + (unsigned)((j & 1) * TILE * 2), j); };
@@ -285,7 +284,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   //
   // p = exp2(s c - m_ref) of the tile, rounded to bf16 into pf, and two
   // partial row sums t of the fp32 p (this lane-half's keys).  s is kept.
-  auto exponentials = [&](float* t) __attribute__((always_inline)) {
+  // hook(i) runs after the i-th group of eight packed values (the loading
+  // group issues its tile loads there).
+  auto exponentials = [&](float* t, auto&& hook) __attribute__((always_inline)) {
     const float neg_m = -m_ref;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -311,6 +312,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
         // the rescale branch that follows (which would keep every p live
         // across it)
         asm volatile("" ::"v"(w[0]), "v"(w[1]), "v"(w[2]), "v"(w[3]));
+        hook(kb * 2 + half);
       }
     }
   };
@@ -336,7 +338,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto phase_y = [&](auto masked_tag, int kv0, auto first_tag) __attribute__((always_inline)) {
+  auto no_hook = [](int) {};
+  auto phase_y = [&](auto masked_tag, int kv0, auto first_tag, auto&& hook) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     constexpr bool FIRST = decltype(first_tag)::value;   // the wave's first tile: m_ref = -inf
     if constexpr (MASKED) {
@@ -362,12 +365,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       // no reference yet: the sums would be inf or NaN, so take the maximum
       // right away
       rescale();
-      exponentials(t);
+      exponentials(t, hook);
     } else {
-      exponentials(t);
+      exponentials(t, hook);
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(!(t[0] + t[1] <= kPMaxBf16)) != 0, 0)) {
         rescale();
-        exponentials(t);
+        exponentials(t, no_hook);
       }
     }
     l_part[0] += t[0];
@@ -434,9 +437,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
       x_end();
       y_start();
       if (first_masked <= 0)
-        phase_y(T_{}, 0, T_{});
+        phase_y(T_{}, 0, T_{}, no_hook);
       else
-        phase_y(F_{}, 0, T_{});
+        phase_y(F_{}, 0, T_{}, no_hook);
       y_end();
       // X_{t-1}, Y_{t-1} (softmax of tile t), unmasked.  At d = 128 the loop
       // is unrolled by two so that each step's buffers are compile-time
@@ -448,11 +451,46 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
         phase_x(T_{}, T_{}, ks_base + (ODD ? TILE : 0), vs_base + (ODD ? 0 : TILE));
         x_end();
         y_start();
-        phase_y(F_{}, t * BC, F_{});
+        phase_y(F_{}, t * BC, F_{}, no_hook);
         y_end();
       };
       int t = 1;
+      // d = 128: steps whose two loads (K_{t+2}, V_{t+1}) are full tiles
+      // inside the work-group's range take them without tests, the global
+      // bases as running pointers: the loading wave issues its vector phase
+      // alone, so each scalar instruction and branch there costs it issue
+      // time.  Each tensor's four loads go out after a group of packed values
+      // (K after the first, V after the second) rather than all at the phase
+      // start: 1.5-3% faster on every d = 128 workload.
+      const int t_fast = LOADER ? min(t_plain, min(n_full, wg_tiles) - 2) : 0;
+      const char* kp = (const char*)kg + (unsigned long long)(unsigned)(t + 2) * tile_bytes;
+      const char* vp = (const char*)vg + (unsigned long long)(unsigned)(t + 1) * tile_bytes;
+      // K_{t+2} goes to buffer t & 1, V_{t+1} to buffer (t + 1) & 1
+      auto fast_step = [&](int t, const __bf16* kt, const __bf16* vt, unsigned lk, unsigned lv)
+                           __attribute__((always_inline)) {
+        phase_x(T_{}, T_{}, kt, vt);
+        x_end();
+        // with no branch here, the scheduler would hoist the softmax above
+        // the barrier into the matrix-core phase
+        __builtin_amdgcn_sched_barrier(0);
+        auto hook = [&](int i) __attribute__((always_inline)) {
+          if (i == 0) load_full(kgo, kp, lk);
+          if (i == 1) load_full(vgo, vp, lv);
+        };
+        phase_y(F_{}, t * BC, F_{}, hook);
+        kp += tile_bytes;
+        vp += tile_bytes;
+        y_end();
+      };
       if constexpr (D == 128) {
+        if constexpr (LOADER) {
+          for (; t + 1 < t_fast; t += 2) {
+            fast_step(t, ks_base + TILE, vs_base, lds_k + lds_wave + TILE * 2,
+                      lds_v + lds_wave);
+            fast_step(t + 1, ks_base, vs_base + TILE, lds_k + lds_wave,
+                      lds_v + lds_wave + TILE * 2);
+          }
+        }
         for (; t + 1 < t_plain; t += 2) {
           plain_step(T_{}, t);
           plain_step(F_{}, t + 1);
@@ -462,11 +500,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
           ++t;
         }
       } else {
+        // (the same fast steps at d = 64, with run-time buffers, measured
+        // 5% slower)
         for (; t < t_plain; ++t) {
           phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
           x_end();
           y_start();
-          phase_y(F_{}, t * BC, F_{});
+          phase_y(F_{}, t * BC, F_{}, no_hook);
           y_end();
         }
       }
@@ -474,7 +514,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
         phase_x(T_{}, T_{}, kt_of(t - 1), vt_of(t - 1));
         x_end();
         y_start();
-        phase_y(T_{}, t * BC, F_{});
+        phase_y(T_{}, t * BC, F_{}, no_hook);
         y_end();
       }
       phase_x(F_{}, T_{}, kt_of(T - 1), vt_of(T - 1));

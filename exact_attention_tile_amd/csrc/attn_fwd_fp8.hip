@@ -184,8 +184,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     const int vk = v_row_key(row);
     k_key[i] = row;
     v_key[i] = vk;
-    kgo[i] = (unsigned)((long long)row * tkv + (pc ^ swz_k8<D>(row)) * 16);
-    vgo[i] = (unsigned)((long long)vk * tkv + (pc ^ swz_v8<D>(row)) * 16);
+    // less 1024 (i % 4): the loads share M0 in groups of four (lds_dma_*);
+    // still >= 0, as load i starts at least that many bytes into the tile
+    kgo[i] = (unsigned)((long long)row * tkv + (pc ^ swz_k8<D>(row)) * 16) - (unsigned)((i & 3) * 1024);
+    vgo[i] = (unsigned)((long long)vk * tkv + (pc ^ swz_v8<D>(row)) * 16) - (unsigned)((i & 3) * 1024);
   }
   const unsigned lds_k = (unsigned)(size_t)((ATTN_LDS unsigned char*)ks_base);
   const unsigned lds_v = (unsigned)(size_t)((ATTN_LDS unsigned char*)vs_base);
@@ -200,20 +202,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_fp8_kernel(FwdParams p) {
     const unsigned la0 = lds_buf + lds_wave;
     const unsigned char* base = src + (unsigned long long)(unsigned)j * tile_bytes;
     if (__builtin_expect(j < n_full, 1)) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(la0 + i * 1024),
-                     "v"(go[i]), "s"(base)
-                     : "memory");
+      lds_dma_tile_s<LPW>(la0, go, base);
     } else {
+      const void* g[LPW];
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const long long back = (long long)(kv0 + key[i] < N ? 0 : kv0 + key[i] - (N - 1)) * tkv;
-        const unsigned char* g = base + (long long)go[i] - back;
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(la0 + i * 1024),
-                     "v"(g)
-                     : "memory");
+        g[i] = base + (long long)go[i] - back;
       }
+      lds_dma_tile_v<LPW>(la0, g);
     }
   };
   auto load_k = [&](int j) { load_tile(kgo, k_key, kg, lds_k + (unsigned)((j & 1) * TILE), j); };

@@ -217,6 +217,89 @@ __device__ __forceinline__ unsigned pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(x, bf16x2));
 }
 
+// ---- LDS-DMA tile loads (global_load_lds_dwordx4) ---------------------------
+// One instruction moves 1 KiB: lane l reads 16 bytes at its global address
+// and writes them to LDS bytes [M0 + imm + 16 l, +16).  The immediate offset
+// imm is added to both the global and the LDS address, so up to four loads
+// (imm = 0, 1024, 2048, 3072) share one M0 value, provided each lane's
+// global offset for load i is stored less 1024 i.  An SALU write of M0
+// needs one wait state before an LDS-DMA instruction reads it (the s_nop).
+// The loads are inline asm so that the compiler does not order them against
+// LDS reads of other buffers; the caller waits for them (vmcnt).
+//
+// lds_dma_s<C>: C loads from the SGPR base plus the lanes' 32-bit offsets
+// go[0..C-1] (go[i] = byte offset - 1024 i), into LDS from m0.
+template <int C>
+__device__ __forceinline__ void lds_dma_s(unsigned m0, const unsigned* go, const void* base) {
+  static_assert(C >= 1 && C <= 4, "one M0 value covers four loads");
+  if constexpr (C == 1) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 ::"s"(m0), "v"(go[0]), "s"(base) : "memory");
+  } else if constexpr (C == 2) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %3\n\t"
+                 "global_load_lds_dwordx4 %2, %3 offset:1024"
+                 ::"s"(m0), "v"(go[0]), "v"(go[1]), "s"(base) : "memory");
+  } else if constexpr (C == 3) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %4\n\t"
+                 "global_load_lds_dwordx4 %2, %4 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %3, %4 offset:2048"
+                 ::"s"(m0), "v"(go[0]), "v"(go[1]), "v"(go[2]), "s"(base) : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %5\n\t"
+                 "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %4, %5 offset:3072"
+                 ::"s"(m0), "v"(go[0]), "v"(go[1]), "v"(go[2]), "v"(go[3]), "s"(base) : "memory");
+  }
+}
+// lds_dma_v<C>: the same from per-lane 64-bit addresses g[i] (each 1024 i
+// bytes below the data it loads).
+template <int C>
+__device__ __forceinline__ void lds_dma_v(unsigned m0, const void* const* g) {
+  static_assert(C >= 1 && C <= 4, "one M0 value covers four loads");
+  if constexpr (C == 1) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 ::"s"(m0), "v"(g[0]) : "memory");
+  } else if constexpr (C == 2) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "global_load_lds_dwordx4 %2, off offset:1024"
+                 ::"s"(m0), "v"(g[0]), "v"(g[1]) : "memory");
+  } else if constexpr (C == 3) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+                 "global_load_lds_dwordx4 %3, off offset:2048"
+                 ::"s"(m0), "v"(g[0]), "v"(g[1]), "v"(g[2]) : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+                 "global_load_lds_dwordx4 %3, off offset:2048\n\t"
+                 "global_load_lds_dwordx4 %4, off offset:3072"
+                 ::"s"(m0), "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]) : "memory");
+  }
+}
+// N loads of one wave (LDS bytes m0 + 1024 i for load i): groups of four,
+// one M0 write per group.
+template <int N, int G = 0>
+__device__ __forceinline__ void lds_dma_tile_s(unsigned m0, const unsigned* go, const void* base) {
+  if constexpr (G < N) {
+    lds_dma_s<(N - G < 4 ? N - G : 4)>(m0 + G * 1024, go + G, base);
+    lds_dma_tile_s<N, G + 4>(m0, go, base);
+  }
+}
+template <int N, int G = 0>
+__device__ __forceinline__ void lds_dma_tile_v(unsigned m0, const void* const* gp) {
+  if constexpr (G < N) {
+    lds_dma_v<(N - G < 4 ? N - G : 4)>(m0 + G * 1024, gp + G);
+    lds_dma_tile_v<N, G + 4>(m0, gp);
+  }
+}
+
 // Host side: enqueues `kernel` on `stream` and returns the status of that
 // launch alone (hipGetLastError would also report an earlier, unrelated
 // failure on the calling thread).  The arguments are taken by value with

@@ -523,7 +523,9 @@ __global__ __launch_bounds__(512, 1) void tile_loads(Stamp* out, float* sink, co
       if constexpr (KIND == 0) {
 #pragma unroll
         for (int i = 0; i < L; ++i)
-          asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0 + i * 1024),
+          // (an SALU write of M0 needs one wait state before the LDS-DMA
+          // load reads it)
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0 + i * 1024),
                        "v"((unsigned)(lane * 16 + i * 1024)), "s"(base)
                        : "memory");
       } else {
