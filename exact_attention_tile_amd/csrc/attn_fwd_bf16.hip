@@ -380,8 +380,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_fwd_bf16_kernel(FwdParams p) 
   // ---- phase schedule ------------------------------------------------------
   // Group A runs X_j in phase 2j+2 and Y_j in phase 2j+3; group B one phase
   // later.  So K_t is read in phases 2t and 2t+1 and V_t in phases 2t+2 and
-  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u at the start of
-  // its vector phase 2u (into buffers last read in phases 2u-2 / 2u-1) and
+  // 2t+3 (from buffer t&1).  Group B loads K_{u+1} and V_u in its vector
+  // phase 2u (into buffers last read in phases 2u-2 / 2u-1) and
   // waits for them at the end of phase 2u+1.  Every wave passes the same
   // number of phase barriers, 2 * wg_tiles + 2.
   //
