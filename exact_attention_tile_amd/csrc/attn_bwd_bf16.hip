@@ -824,11 +824,14 @@ __global__ __launch_bounds__(512, 1) void attn_bwd_dkdv_pair_kernel(BwdParams p)
   TileLoader<D, KW, BQ> ld;
   ld.init(kgrp, lane, tok);
   const unsigned lds_dst = (unsigned)(size_t)((ATTN_LDS __bf16*)(lr ? gsm : qsm));
-  const int nbuf = lr ? 2 : NB;
   float row_val = 0.f;
   auto load_tile = [&](int u) {
     const int q0t = (first + u) * BQ;
-    ld.load(src, tok, lds_dst + (unsigned)((u % nbuf) * TILE * 2), q0t, N);
+    // the buffer: u mod 2 (dO) or u mod NB (Q), each with a constant
+    // divisor (a run-time one costs a full integer division, VALU
+    // reciprocal included, in the loading wave's vector phase)
+    const int slot = lr ? (u & 1) : (u % NB);
+    ld.load(src, tok, lds_dst + (unsigned)(slot * TILE * 2), q0t, N);
     if (kgrp == 0) row_val = rsrc[min(q0t + lane, N - 1)];
   };
   auto store_rowv = [&](int u) {
